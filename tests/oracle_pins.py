@@ -1,0 +1,704 @@
+"""Pins of the CPU oracle to what the pages and the mathematics fix.
+
+Every ``pin_*`` function takes an ``oracle.Oracle`` and raises ``AssertionError``
+when the oracle disagrees.  None of them re-derives an expected value by
+calling the oracle on the same question: expected values come from the pages
+(golden fixtures under ``tests/golden/``, each with its citation), from closed
+forms built into the inputs (power-of-two scales, exact multiples of a scale),
+from invariants (error bounds, extreme values), or from independent library
+routines (numpy / torch IEEE conversions, float64 reciprocals).
+
+The same functions are run against deliberately broken builds of the oracle
+(``test_oracle_mutants.py``) to show that a plausible mistake fails at least
+one of them.
+"""
+import os
+import re
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TILE = 2048
+BLOCK = 32
+BITS = (3, 4, 8)
+DTYPES = ("fp16", "bf16")
+
+
+# ---------------------------------------------------------------------------
+# independent helpers (layout rule and IEEE conversions, not the oracle's code)
+# ---------------------------------------------------------------------------
+
+def qmax(bits):
+    return 1 << (bits - 1)
+
+
+def tile_bytes(bits):
+    return TILE * bits // 8 + 2 * (TILE // BLOCK)
+
+
+def scale_offset(bits):
+    return TILE * bits // 8
+
+
+def unpack(bits, packed):
+    """Codes (T, 2048) and raw fp16 scale bits (T, 64) from packed tiles."""
+    t = np.asarray(packed, np.uint8).reshape(-1, tile_bytes(bits))
+    so = scale_offset(bits)
+    scales = t[:, so:so + 128].copy().view("<u2")
+    if bits == 8:
+        codes = t[:, :2048].astype(np.int64)
+    elif bits == 4:
+        words = t[:, :1024].copy().view("<u4").astype(np.int64)          # (T, 256)
+        codes = (words[:, :, None] >> (4 * np.arange(8))) & 15          # (T, 256, 8)
+        codes = codes.reshape(-1, 2048)
+    else:
+        q2 = t[:, :512].copy().view("<u2").astype(np.int64)             # (T, 256)
+        q1 = t[:, 512:768].astype(np.int64)                             # (T, 256)
+        low = (q2[:, :, None] >> (2 * np.arange(8))) & 3
+        high = (q1[:, :, None] >> np.arange(8)) & 1
+        codes = (low | (high << 2)).reshape(-1, 2048)
+    return codes, scales
+
+
+def pack(bits, codes, scale_bits):
+    """Packed tiles from codes (T, 2048) and fp16 scale bits (T, 64), by the layout rule."""
+    codes = np.asarray(codes, np.int64).reshape(-1, 2048)
+    T = codes.shape[0]
+    out = np.zeros((T, tile_bytes(bits)), np.uint8)
+    if bits == 8:
+        out[:, :2048] = codes
+    elif bits == 4:
+        c = codes.reshape(T, 256, 8)
+        words = np.zeros((T, 256), np.uint32)
+        for j in range(8):
+            words |= (c[:, :, j] << (4 * j)).astype(np.uint32)
+        out[:, :1024] = words.view(np.uint8).reshape(T, 1024)
+    else:
+        c = codes.reshape(T, 256, 8)
+        q2 = np.zeros((T, 256), np.uint16)
+        q1 = np.zeros((T, 256), np.uint8)
+        for j in range(8):
+            q2 |= ((c[:, :, j] & 3) << (2 * j)).astype(np.uint16)
+            q1 |= (((c[:, :, j] >> 2) & 1) << j).astype(np.uint8)
+        out[:, :512] = q2.view(np.uint8).reshape(T, 512)
+        out[:, 512:768] = q1
+    so = scale_offset(bits)
+    out[:, so:so + 128] = np.asarray(scale_bits, np.uint16).reshape(T, 64).view(np.uint8).reshape(T, 128)
+    return out.ravel()
+
+
+def f16_bits(x):
+    return np.asarray(x, np.float64).astype(np.float16).view(np.uint16)
+
+
+def f16_value(b):
+    return np.asarray(b, np.uint16).view(np.float16).astype(np.float64)
+
+
+def bf16_value(b):
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_bits(x):
+    """Nearest bfloat16 (ties to even) of float64 values, via torch's conversion."""
+    import torch
+    t = torch.from_numpy(np.asarray(x, np.float64).astype(np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def dtype_bits(dtype, x):
+    """dtype bit patterns of float64 values that are exact in binary32."""
+    x = np.asarray(x, np.float64)
+    assert np.all(x.astype(np.float32).astype(np.float64) == x)
+    return f16_bits(x) if dtype == "fp16" else bf16_bits(x)
+
+
+def dtype_value(dtype, b):
+    return f16_value(b) if dtype == "fp16" else bf16_value(b)
+
+
+def pow2_f16_bits(k):
+    """fp16 bits of 2^k built from the format fields (normal or subnormal)."""
+    if k >= -14:
+        return (k + 15) << 10
+    return 1 << (k + 24)
+
+
+def all_finite(dtype):
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = dtype_value(dtype, b)
+    keep = np.isfinite(v)
+    return b[keep], v[keep]
+
+
+def pad_tiles(blocks):
+    """Stack (nb, 32) blocks into whole tiles (nb rounded up to 64 blocks with zeros)."""
+    nb = blocks.shape[0]
+    nt = -(-nb // 64)
+    out = np.zeros((nt * 64, BLOCK), blocks.dtype)
+    out[:nb] = blocks
+    return out.reshape(-1)
+
+
+def read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ---------------------------------------------------------------------------
+# P1: tile byte counts printed on the page
+# ---------------------------------------------------------------------------
+
+def pin_tile_bytes(o):
+    for fmt, n, nbytes in read_golden("tile_bytes.txt"):
+        bits = {"INT4": 4, "INT3": 3}[fmt]
+        assert o.packed_bytes(bits, int(n)) == int(nbytes), (fmt, o.packed_bytes(bits, int(n)))
+        for t in (1, 3, 64):
+            assert o.packed_bytes(bits, t * int(n)) == t * int(nbytes)
+    # INT8 extends the same framework (2048 B of codes + 128 B of scales).
+    assert o.packed_bytes(8, 2048) == 2176
+    for bits in BITS:
+        assert o.packed_bytes(bits, 2047) == 0 and o.packed_bytes(bits, 2048 + 32) == 0
+    # and the buffer the oracle writes has exactly that size
+    for bits in BITS:
+        p = o.encode(bits, "fp16", np.zeros(4096, np.uint16))
+        assert p.size == 2 * tile_bytes(bits)
+
+
+# ---------------------------------------------------------------------------
+# P6: bit order inside a unit and scale placement
+# ---------------------------------------------------------------------------
+
+def _block_with_codes(bits, codes8, s=1.0):
+    """32 values whose block quantizes to `codes8` in unit 0 (scale s exactly).
+
+    Unit 1 holds the anchor -Q*s (code 0) so the block maximum is Q*s."""
+    Q = qmax(bits)
+    k = np.zeros(BLOCK, np.float64)
+    k[:8] = np.asarray(codes8, np.float64) - Q
+    k[8] = -Q
+    return k * s
+
+
+def pin_unit_bit_order(o):
+    for row in read_golden("unit_bit_order.txt"):
+        fmt, codes = row[0], [int(c) for c in row[1].split(",")]
+        expect = dict(kv.split("=") for kv in row[2:])
+        bits = {"INT4": 4, "INT3": 3}[fmt]
+        for dtype in DTYPES:
+            x = np.zeros(TILE, np.float64)
+            x[:BLOCK] = _block_with_codes(bits, codes)
+            p = o.encode(bits, dtype, dtype_bits(dtype, x))
+            if bits == 4:
+                word = int(p[0:4].view("<u4")[0])
+                assert word == int(expect["word"], 16), (dtype, codes, hex(word))
+            else:
+                q2 = int(p[0:2].view("<u2")[0])
+                q1 = int(p[512])
+                assert q2 == int(expect["q2"], 16), (dtype, codes, hex(q2))
+                assert q1 == int(expect["q1"], 16), (dtype, codes, hex(q1))
+
+
+def pin_scale_placement(o):
+    """Block g's scale sits at scale_offset + 2g, little-endian fp16."""
+    for bits in BITS:
+        Q = qmax(bits)
+        for dtype in DTYPES:
+            x = np.zeros((2 * 64, BLOCK), np.float64)
+            exps = np.array([(g * 7) % 21 - 12 for g in range(128)])
+            for g in range(128):
+                s = 2.0 ** exps[g]
+                x[g, g % BLOCK] = -Q * s           # anchor at a varying position
+                x[g, (g + 5) % BLOCK] = (Q - 1) * s
+            p = o.encode(bits, dtype, dtype_bits(dtype, x.ravel()))
+            codes, scales = unpack(bits, p)
+            want = np.array([pow2_f16_bits(int(e)) for e in exps], np.uint16).reshape(2, 64)
+            assert np.array_equal(scales, want), (bits, dtype)
+            c = codes.reshape(128, BLOCK)
+            for g in range(128):
+                assert c[g, g % BLOCK] == 0 and c[g, (g + 5) % BLOCK] == 2 * Q - 1
+            # every other position in each block decodes to zero -> code Q
+            mask = np.ones((128, BLOCK), bool)
+            mask[np.arange(128), np.arange(128) % BLOCK] = False
+            mask[np.arange(128), (np.arange(128) + 5) % BLOCK] = False
+            assert np.all(c[mask] == Q)
+
+
+# ---------------------------------------------------------------------------
+# P3: exact round trip of multiples k*s of a representable scale
+# ---------------------------------------------------------------------------
+
+def _exact_scales(bits, dtype):
+    """Scales s (fp16 values) such that every k*s, |k| <= Q, is exact in dtype."""
+    Q = qmax(bits)
+    sig = 11 if dtype == "fp16" else 8
+    kbits = max(1, (Q - 1).bit_length())   # |k| <= Q-1 needs this many bits; Q itself is a power of 2
+    out = []
+    for m in (1, 3, 5, 7):
+        if m.bit_length() + kbits > sig:
+            continue
+        for e in (-20, -12, -5, 0, 3):
+            s = m * 2.0 ** e
+            if Q * s > 60000 or s < 2.0 ** -14:
+                continue
+            out.append(s)
+    return out
+
+
+def pin_exact_roundtrip(o, seed=1):
+    rng = np.random.default_rng(seed)
+    for bits in BITS:
+        Q = qmax(bits)
+        for dtype in DTYPES:
+            scales = _exact_scales(bits, dtype)
+            nb = 64 * 3
+            k = rng.integers(-Q, Q, size=(nb, BLOCK))
+            k[np.arange(nb), rng.integers(0, BLOCK, nb)] = -Q          # anchor
+            s = np.array([scales[i % len(scales)] for i in range(nb)])
+            x = (k * s[:, None]).ravel()
+            xb = dtype_bits(dtype, x)
+            p = o.encode(bits, dtype, xb)
+            codes, sb = unpack(bits, p)
+            assert np.array_equal(codes.reshape(nb, BLOCK), k + Q), (bits, dtype)
+            assert np.array_equal(sb.ravel(), f16_bits(s)), (bits, dtype)
+            y = o.decode(bits, dtype, p, x.size)
+            assert np.array_equal(y, xb), (bits, dtype)
+            yf = o.decode_f32(bits, p, x.size)
+            assert np.array_equal(yf.astype(np.float64), x), (bits, dtype)
+
+
+# ---------------------------------------------------------------------------
+# P2: extreme values land on the ends of the code range
+# ---------------------------------------------------------------------------
+
+def pin_extremes_and_grid(o, seed=2):
+    """The block's largest |x| maps to code 0 (negative) or 2Q-1 (positive), and
+    every decoded value is an integer in [-Q, Q-1] times the block scale."""
+    rng = np.random.default_rng(seed)
+    for bits in BITS:
+        Q = qmax(bits)
+        for dtype in DTYPES:
+            nb = 64 * 4
+            x = rng.standard_normal((nb, BLOCK)) * np.exp(rng.uniform(-3, 6, size=(nb, 1)))
+            xb = dtype_bits(dtype, x.astype(np.float32).astype(np.float64)) if dtype == "bf16" else \
+                f16_bits(x)
+            xv = dtype_value(dtype, xb).reshape(nb, BLOCK)
+            p = o.encode(bits, dtype, xb)
+            codes, sb = unpack(bits, p)
+            codes = codes.reshape(nb, BLOCK)
+            d = f16_value(sb.ravel())
+            # only blocks whose scale is a normal fp16 value (full relative precision)
+            ok = d >= 2.0 ** -14
+            assert ok.mean() > 0.9
+            i = np.argmax(np.abs(xv), axis=1)
+            ext = codes[np.arange(nb), i]
+            neg = xv[np.arange(nb), i] < 0
+            assert np.all(ext[neg & ok] == 0) and np.all(ext[~neg & ok] == 2 * Q - 1), (bits, dtype)
+            assert np.all((codes >= 0) & (codes <= 2 * Q - 1))
+            y = o.decode_f32(bits, p, nb * BLOCK).astype(np.float64).reshape(nb, BLOCK)
+            kk = y[ok] / d[ok, None]
+            assert np.array_equal(kk, (codes - Q)[ok]), (bits, dtype)
+
+
+# ---------------------------------------------------------------------------
+# P4: zero, tiny and huge blocks
+# ---------------------------------------------------------------------------
+
+def pin_zero_tiny_huge(o):
+    for bits in BITS:
+        Q = qmax(bits)
+        for dtype in DTYPES:
+            # all +0 / -0
+            xb = np.zeros(TILE, np.uint16)
+            xb[1::2] = 0x8000
+            p = o.encode(bits, dtype, xb)
+            codes, sb = unpack(bits, p)
+            assert np.all(codes == Q) and np.all(sb == 0)
+            assert np.all(o.decode(bits, dtype, p, TILE) == 0)       # +0 everywhere
+        # bf16 blocks whose m/Q is below half the smallest fp16 subnormal flush to 0
+        tiny = np.zeros(TILE, np.float64)
+        tiny[:BLOCK] = 2.0 ** -130 * np.sign(np.arange(BLOCK) - 15.5)
+        tiny[BLOCK] = Q * 2.0 ** -25                              # m/Q = 2^-25: tie -> 0
+        tiny[2 * BLOCK] = Q * 2.0 ** -25 * (1 + 2.0 ** -7)        # just above: -> 2^-24
+        tiny[2 * BLOCK + 1] = -Q * 2.0 ** -25 * (1 + 2.0 ** -7)
+        p = o.encode(bits, "bf16", dtype_bits("bf16", tiny))
+        codes, sb = unpack(bits, p)
+        assert sb[0, 0] == 0 and sb[0, 1] == 0 and sb[0, 2] == 0x0001, sb[0, :3]
+        assert np.all(codes[0, :2 * BLOCK] == Q)
+        # scale 2^-24, multiplier 2^24: the values scale to +-(Q/2)(1 + 2^-7)
+        half = np.rint(Q / 2 * (1 + 2.0 ** -7))
+        assert codes[0, 2 * BLOCK] == Q + half and codes[0, 2 * BLOCK + 1] == Q - half
+        # bf16 block far above 65504*Q saturates the scale at 65504
+        huge = np.zeros(TILE, np.float64)
+        huge[:4] = [2.0 ** 24, -2.0 ** 24, 65504.0, -65504.0]
+        p = o.encode(bits, "bf16", dtype_bits("bf16", huge))
+        codes, sb = unpack(bits, p)
+        assert sb[0, 0] == 0x7BFF
+        assert codes[0, 0] == 2 * Q - 1 and codes[0, 1] == 0
+        assert codes[0, 2] == Q + 1 and codes[0, 3] == Q - 1
+
+
+# ---------------------------------------------------------------------------
+# P5: brute force over tiny blocks with a power-of-two scale
+# ---------------------------------------------------------------------------
+
+def _pow2_exponents(bits):
+    Q = qmax(bits)
+    top = 15 - (bits - 1)          # Q * 2^k must stay a finite fp16 value
+    return [-24, -20, -14, -9, -1, 0, 3, top]
+
+
+def pin_bruteforce_pow2(o, stride=1):
+    """Every finite dtype value x with |x| <= Q*2^k in the block [-Q*2^k, x, 0...]:
+    the scale is 2^k, the multiplier 2^-k, so the code is the closed form
+    clip(round_half_even(x / 2^k), -Q, Q-1) + Q, evaluated exactly in float64."""
+    for bits in BITS:
+        Q = qmax(bits)
+        for dtype in DTYPES:
+            allb, allv = all_finite(dtype)
+            for k in _pow2_exponents(bits):
+                a = Q * 2.0 ** k
+                sel = np.abs(allv) <= a
+                xb, xv = allb[sel][::stride], allv[sel][::stride]
+                nb = xb.size
+                blocks = np.zeros((nb, BLOCK), np.uint16)
+                blocks[:, 0] = dtype_bits(dtype, np.array([-a]))[0]
+                blocks[:, 1] = xb
+                p = o.encode(bits, dtype, pad_tiles(blocks))
+                codes, sb = unpack(bits, p)
+                codes = codes.reshape(-1, BLOCK)[:nb]
+                want = np.clip(np.rint(xv / 2.0 ** k), -Q, Q - 1) + Q
+                bad = codes[:, 1] != want
+                assert not bad.any(), (bits, dtype, k, xv[bad][:4], codes[bad, 1][:4], want[bad][:4])
+                assert np.all(codes[:, 0] == 0)
+                assert np.all(sb.ravel()[:nb] == pow2_f16_bits(k))
+
+
+def pin_bruteforce_general_scale(o):
+    """Blocks [-Q*d, x, 0...] with d a non-power-of-two fp16 value and every
+    finite fp16 x with |x| <= Q*d.  The scale is d exactly and the encode
+    multiplier e = RN32(1/d) (the reading that the page's encode scale is a
+    multiplier kept in fp32).  The code is clip(round_half_even(RN32(x*e))) + Q,
+    with x*e formed exactly in float64 and rounded once to float32.  Some x lie
+    where x*e and x/d round to different codes (for scales such as 0x0F90,
+    0x17A8, 0x3368), so the check also separates "multiply by e" from "divide by d"."""
+    allb, allv = all_finite("fp16")
+    for bits in BITS:
+        Q = qmax(bits)
+        diff_seen = 0
+        for d_bits in (0x3555, 0x2E66, 0x3BFF, 0x0F90, 0x17A8, 0x3368, 0x0123):
+            d = float(f16_value(np.uint16(d_bits)))
+            a = Q * d
+            if f16_value(f16_bits(a)) != a:
+                continue
+            sel = np.abs(allv) <= a
+            xb, xv = allb[sel], allv[sel]
+            nb = xb.size
+            blocks = np.zeros((nb, BLOCK), np.uint16)
+            blocks[:, 0] = f16_bits(-a)
+            blocks[:, 1] = xb
+            p = o.encode(bits, "fp16", pad_tiles(blocks))
+            codes, sb = unpack(bits, p)
+            codes = codes.reshape(-1, BLOCK)[:nb]
+            assert np.all(sb.ravel()[:nb] == d_bits)
+            e = np.float64(np.float32(1.0 / d))
+            v = (xv * e).astype(np.float32).astype(np.float64)
+            want = np.clip(np.rint(v), -Q, Q - 1) + Q
+            bad = codes[:, 1] != want
+            assert not bad.any(), (bits, hex(d_bits), xv[bad][:4], codes[bad, 1][:4], want[bad][:4])
+            by_div = np.clip(np.rint((xv / d).astype(np.float32).astype(np.float64)), -Q, Q - 1) + Q
+            diff_seen += int((by_div != want).sum())
+        assert diff_seen > 0, bits
+
+
+def pin_scale_reciprocal_exhaustive(o):
+    """For every positive finite fp16 d: a block maximum of Q*d gives scale d and
+    multiplier RN32(1/d), taken from a float64 division rounded once to float32
+    (double rounding is harmless here: 53 >= 2*24 + 2)."""
+    d_bits = np.arange(1, 0x7C00, dtype=np.uint16)
+    d = f16_value(d_bits)
+    for bits in BITS:
+        Q = qmax(bits)
+        for i in range(0, d_bits.size, 1):
+            db, e = o.block_scale(bits, float(np.float32(Q * d[i])))
+            if db != d_bits[i] or e != np.float32(1.0 / d[i]):
+                raise AssertionError((bits, hex(int(d_bits[i])), hex(db), e, np.float32(1.0 / d[i])))
+        assert o.block_scale(bits, 0.0) == (0, 0.0)
+        db, e = o.block_scale(bits, 65504.0 * Q * 4)
+        assert db == 0x7BFF and e == np.float32(1.0 / 65504.0)
+        # arbitrary maxima: scale = nearest fp16 of m/Q (numpy's correctly rounded conversion)
+        rng = np.random.default_rng(bits)
+        ms = (rng.standard_normal(2000) * np.exp(rng.uniform(-20, 12, 2000))).astype(np.float32)
+        for m in np.abs(ms):
+            db, _ = o.block_scale(bits, float(m))
+            want = f16_bits(np.float64(m) / Q)
+            if float(m) / Q > 65504:
+                want = np.uint16(0x7BFF)
+            assert db == want, (bits, m, hex(db), hex(int(want)))
+
+
+# ---------------------------------------------------------------------------
+# IEEE conversions against numpy / torch
+# ---------------------------------------------------------------------------
+
+def _f32_probe_values(seed=3):
+    rng = np.random.default_rng(seed)
+    bitsr = rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    rnd = bitsr.view(np.float32)
+    rnd = rnd[np.isfinite(rnd)]
+    # values near every fp16 value and every midpoint between neighbours
+    b16, v16 = all_finite("fp16")
+    v16 = np.sort(np.unique(v16))
+    mids = (v16[:-1] + v16[1:]) / 2                       # exact in float64; exact in f32 too
+    near = np.concatenate([v16, mids]).astype(np.float32)
+    up = np.nextafter(near, np.float32(np.inf))
+    dn = np.nextafter(near, np.float32(-np.inf))
+    special = np.array([0.0, -0.0, 65504, 65519.99, 65520, 65536, 1e30, 2.0 ** -25, 2.0 ** -24,
+                        2.0 ** -25 * 1.5, 2.0 ** -14, 2.0 ** -149, 3.4e38], np.float32)
+    return np.concatenate([rnd, near, up, dn, special, -special])
+
+
+def pin_f16_conversions(o):
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = o.f16_to_f32(b)
+    want = b.view(np.float16).astype(np.float32)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+    x = _f32_probe_values()
+    got = o.f32_to_f16(x)
+    want = x.astype(np.float16).view(np.uint16)
+    bad = got != want
+    assert not bad.any(), (x[bad][:5], got[bad][:5], want[bad][:5])
+
+
+def pin_bf16_conversions(o):
+    import torch
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = o.bf16_to_f32(b)
+    want = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).float().numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+    x = _f32_probe_values(4)
+    xb = np.concatenate([x, (x.view(np.uint32) & 0xFFFF0000 | 0x8000).view(np.float32)])  # bf16 ties
+    xb = xb[np.isfinite(xb)]
+    got = o.f32_to_bf16(xb)
+    want = torch.from_numpy(xb).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    bad = got != want
+    assert not bad.any(), (xb[bad][:5], got[bad][:5], want[bad][:5])
+
+
+# ---------------------------------------------------------------------------
+# decode rounding to the I/O dtype
+# ---------------------------------------------------------------------------
+
+def pin_decode_rounding(o, seed=5):
+    """decode = dtype_RNE((code - Q) * scale) for arbitrary codes and scales,
+    the product evaluated exactly in float64, the rounding by numpy / torch."""
+    rng = np.random.default_rng(seed)
+    for bits in BITS:
+        Q = qmax(bits)
+        T = 4
+        codes = rng.integers(0, 2 * Q, size=(T, 2048))
+        sbits = rng.integers(0, 0x7C00, size=(T, 64)).astype(np.uint16)
+        p = pack(bits, codes, sbits)
+        exact = (codes - Q).reshape(T, 64, BLOCK) * f16_value(sbits)[:, :, None]
+        exact = exact.ravel()
+        yf = o.decode_f32(bits, p, T * 2048).astype(np.float64)
+        assert np.array_equal(yf, exact), bits
+        for dtype in DTYPES:
+            y = o.decode(bits, dtype, p, T * 2048)
+            want = f16_bits(exact) if dtype == "fp16" else bf16_bits(exact)
+            assert np.array_equal(y, want), (bits, dtype)
+
+
+# ---------------------------------------------------------------------------
+# P7: reduction special cases
+# ---------------------------------------------------------------------------
+
+def _rng_blocks(rng, dtype, nb, scale_lo=-4, scale_hi=4):
+    x = rng.standard_normal((nb, BLOCK)) * np.exp(rng.uniform(scale_lo, scale_hi, size=(nb, 1)))
+    x[rng.random((nb, BLOCK)) < 0.01] *= 50
+    return dtype_bits(dtype, x.astype(np.float32).astype(np.float64)).ravel() if dtype == "bf16" \
+        else f16_bits(x).ravel()
+
+
+def pin_reduce_r1_composition(o, seed=6):
+    """R = 1: the reduction re-quantizes dtype_RNE(exact decode) and decodes it.
+    The packed result equals encoding the decoded-and-rounded values (rounding by
+    numpy / torch); the output equals dtype_RNE((code-Q)*scale) of that result."""
+    rng = np.random.default_rng(seed)
+    for bits in BITS:
+        Q = qmax(bits)
+        for dtype in DTYPES:
+            n = 2 * TILE
+            xb = _rng_blocks(rng, dtype, n // BLOCK)
+            p = o.encode(bits, dtype, xb)
+            codes, sb = unpack(bits, p)
+            exact = ((codes - Q).reshape(-1, 64, BLOCK) * f16_value(sb)[:, :, None]).ravel()
+            zb = f16_bits(exact) if dtype == "fp16" else bf16_bits(exact)
+            want_packed = o.encode(bits, dtype, zb)
+            out, y = o.reduce(bits, dtype, [p], n)
+            assert np.array_equal(out, want_packed), (bits, dtype)
+            c2, s2 = unpack(bits, out)
+            ex2 = ((c2 - Q).reshape(-1, 64, BLOCK) * f16_value(s2)[:, :, None]).ravel()
+            want_y = f16_bits(ex2) if dtype == "fp16" else bf16_bits(ex2)
+            assert np.array_equal(y, want_y), (bits, dtype)
+
+
+def pin_reduce_exact_common_scale(o, seed=7):
+    """All ranks of a block share a scale s; every element's integer sum stays in
+    [-Q, Q-1] and one element sums to -Q.  Then every partial sum is exact, the
+    summed block has scale s again, and the output equals the exact sum."""
+    rng = np.random.default_rng(seed)
+    for bits in BITS:
+        Q = qmax(bits)
+        for dtype in DTYPES:
+            scales = _exact_scales(bits, dtype)
+            for R in (1, 2, 3, 4, 8):
+                nb = 128
+                k = np.zeros((R, nb, BLOCK), np.int64)
+                for b in range(nb):
+                    for r in range(R):
+                        k[r, b, r] = -Q                       # rank r's anchor at element r
+                        k[(r + 1) % R, b, r] += Q - 1 if R > 1 else 0   # keeps element r's sum at -1 (R>1)
+                    # element R sums to exactly -Q
+                    if R == 1:
+                        k[0, b, R] = -Q
+                    else:
+                        k[0, b, R] = -(Q // 2)
+                        k[1, b, R] = -(Q // 2)
+                    # the rest: random sums in [-Q, Q-1] split over the ranks
+                    for e in range(R + 1, BLOCK):
+                        tot = int(rng.integers(-Q, Q))
+                        parts = np.zeros(R, np.int64)
+                        left = tot
+                        for r in range(R - 1):
+                            lo, hi = max(-Q, left - (Q - 1) * (R - 1 - r)), min(Q - 1, left + Q * (R - 1 - r))
+                            parts[r] = int(rng.integers(lo, hi + 1))
+                            left -= parts[r]
+                        parts[R - 1] = left
+                        k[:, b, e] = parts
+                assert np.all((k >= -Q) & (k <= Q - 1))
+                tot = k.sum(axis=0)
+                assert np.all((tot >= -Q) & (tot <= Q - 1)) and np.all((tot == -Q).any(axis=1))
+                s = np.array([scales[i % len(scales)] for i in range(nb)])
+                ranks = [o.encode(bits, dtype, dtype_bits(dtype, (k[r] * s[:, None]).ravel()))
+                         for r in range(R)]
+                out, y = o.reduce(bits, dtype, ranks, nb * BLOCK)
+                codes, sb = unpack(bits, out)
+                assert np.array_equal(codes.reshape(nb, BLOCK), tot + Q), (bits, dtype, R)
+                assert np.array_equal(sb.ravel(), f16_bits(s)), (bits, dtype, R)
+                assert np.array_equal(y, dtype_bits(dtype, (tot * s[:, None]).ravel())), (bits, dtype, R)
+
+
+def _golden_expect(name):
+    rows = read_golden(name)
+    scale = int(rows[0][1], 16)
+    elems = {r[0]: (int(r[1]), int(r[2], 16)) for r in rows[1:]}
+    return scale, elems
+
+
+def pin_reduce_rank_order(o):
+    scale, elems = _golden_expect("reduce_rank_order.txt")
+    A, B, E2, E3 = 0, 1, 2, 3
+    vals = np.zeros((4, TILE), np.float64)
+    vals[0, [A, E2, E3]] = [-16, 2, 14]
+    vals[1, [A, B]] = [-2.0 ** -20, -2.0 ** -17]
+    vals[2, [A, E2, E3]] = [14, -16, 2]
+    vals[3, [A, E2, E3]] = [2, 14, -16]
+    ranks = [o.encode(4, "fp16", f16_bits(v)) for v in vals]
+    out, y = o.reduce(4, "fp16", ranks, TILE)
+    codes, sb = unpack(4, out)
+    assert sb[0, 0] == scale, hex(sb[0, 0])
+    for name, idx in (("A", A), ("B", B), ("E2", E2), ("E3", E3)):
+        code, ybits = elems[name]
+        assert codes[0, idx] == code, (name, codes[0, idx])
+        assert y[idx] == ybits, (name, hex(y[idx]))
+    assert np.all(codes[0, 4:BLOCK] == 8)
+
+
+def pin_reduce_exact_terms(o):
+    scale, elems = _golden_expect("reduce_exact_terms.txt")
+    c0 = np.full((1, 2048), 128)
+    c1 = np.full((1, 2048), 128)
+    s0 = np.zeros((1, 64), np.uint16)
+    s1 = np.zeros((1, 64), np.uint16)
+    c0[0, 0], s0[0, 0] = 255, 0x3FFF
+    c1[0, 0], s1[0, 0] = 2, 0x4004
+    ranks = [pack(8, c0, s0), pack(8, c1, s1)]
+    out, y = o.reduce(8, "fp16", ranks, TILE)
+    codes, sb = unpack(8, out)
+    assert sb[0, 0] == scale, hex(sb[0, 0])
+    code, ybits = elems["0"]
+    assert codes[0, 0] == code and y[0] == ybits, (codes[0, 0], hex(y[0]))
+    assert np.all(codes[0, 1:] == 128) and np.all(y[1:] == 0)
+
+
+# ---------------------------------------------------------------------------
+# P8: error bound of encode -> reduce -> decode against the exact sum
+# ---------------------------------------------------------------------------
+
+def _ulp(dtype, v):
+    """Spacing of the dtype's values at |v| (normal and subnormal range)."""
+    sig, emin = (11, -14) if dtype == "fp16" else (8, -126)
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** emin)))
+    return 2.0 ** (e - (sig - 1))
+
+
+def pin_error_bound(o, seed=8):
+    rng = np.random.default_rng(seed)
+    for bits in BITS:
+        Q = qmax(bits)
+        c = 1 + Q / 2048 + 1e-6        # worst case per value, in units of the block scale
+        for dtype in DTYPES:
+            for R in (1, 2, 4, 8):
+                n = 2 * TILE
+                xs = [_rng_blocks(rng, dtype, n // BLOCK, -3, 3) for _ in range(R)]
+                xv = [dtype_value(dtype, xb) for xb in xs]
+                ranks = [o.encode(bits, dtype, xb) for xb in xs]
+                out, y = o.reduce(bits, dtype, ranks, n)
+                exact = np.sum(xv, axis=0)
+                d_in = [f16_value(unpack(bits, p)[1]).repeat(BLOCK, axis=1).ravel() for p in ranks]
+                d_out = f16_value(unpack(bits, out)[1]).repeat(BLOCK, axis=1).ravel()
+                absy = np.sum([np.abs(v) for v in xv], axis=0) + np.sum(d_in, axis=0) * Q
+                e1 = c * np.sum(d_in, axis=0) + R * Q * 2.0 ** -24   # input quantization
+                e2 = R * 2.0 ** -24 * absy                           # fp32 rank-order sum
+                big = np.abs(exact) + e1 + e2
+                e3 = _ulp(dtype, big)                                # sum rounded to dtype
+                e4 = c * d_out + Q * 2.0 ** -24                      # re-quantization
+                e5 = _ulp(dtype, big + e3 + e4)                      # output rounded to dtype
+                bound = e1 + e2 + e3 + e4 + e5
+                yv = dtype_value(dtype, y)
+                err = np.abs(yv - exact)
+                bad = err > bound
+                assert not bad.any(), (bits, dtype, R, err[bad][:4], bound[bad][:4])
+                # and the bound is not vacuous: the error is typically far below it
+                assert np.median(err / bound) < 0.6
+
+
+ALL_PINS = [
+    pin_tile_bytes,
+    pin_unit_bit_order,
+    pin_scale_placement,
+    pin_exact_roundtrip,
+    pin_extremes_and_grid,
+    pin_zero_tiny_huge,
+    pin_bruteforce_pow2,
+    pin_bruteforce_general_scale,
+    pin_scale_reciprocal_exhaustive,
+    pin_f16_conversions,
+    pin_bf16_conversions,
+    pin_decode_rounding,
+    pin_reduce_r1_composition,
+    pin_reduce_exact_common_scale,
+    pin_reduce_rank_order,
+    pin_reduce_exact_terms,
+    pin_error_bound,
+]
