@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Throughput of encode -> compressed-domain reduce -> decode on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: R encodes (one per simulated rank, qr_encode) and one
+fused qr_reduce_compressed that decodes the R packed buffers, sums them in
+fp32 in rank order, re-encodes the sum and decodes it.  For the encode/decode
+only workload a step is one qr_encode and one qr_decode.
+
+The reported value is GB/s of FP16 input: R * n * 2 bytes per step divided by
+the step time.  Alongside: the pipeline's algorithmic HBM bytes as % of the
+MI355X peak (8 TB/s), the dominant kernel's roofline (average launch duration
+from HIP events on the launch stream), and the CPU oracle timed on a bounded
+sample of the same input.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GB/s of FP16 input through encode+compressed-reduce+decode; % HBM peak"
+PEAK_HBM_GBS = 8000.0
+TILE_BYTES = {"int3": 896, "int4": 1152, "int8": 2176}
+KERNEL_SOURCES = ["bit_quantized_all_amd/csrc/qr_kernels.hip", "bit_quantized_all_amd/csrc/qr_codec.hpp"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w):
+    """Bytes each kernel must move per launch (compressed buffers in HBM are the wire)."""
+    c = TILE_BYTES[w.fmt] / 2048
+    n = w.n
+    out = {"encode": n * (2 + c), "decode": n * (c + 2)}
+    out["reduce"] = n * (w.ranks * c + c + 2)
+    return out
+
+
+def traffic_from_profiles(kernel):
+    """Measured HBM bytes per launch from the committed counter summary, or None
+    when it is absent or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch", {}).get(kernel)
+
+
+def cpu_baseline(w, xs, out, y, seconds):
+    """The oracle (single-threaded C) on consecutive tiles of every rank, from
+    the first, until about `seconds` of oracle time; each chunk's inputs are
+    copied to the host outside the timed calls, and its outputs are compared
+    with the GPU's bytes for the same tiles."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    o = oracle.default()
+    bits = {"int3": 3, "int4": 4, "int8": 8}[w.fmt]
+    tb = TILE_BYTES[w.fmt]
+    ntiles = w.n // 2048
+    chunk = 16
+    done = 0
+    ok = True
+    busy = 0.0
+    while done + chunk <= ntiles and (busy < seconds or done == 0):
+        sv = slice(done * 2048, (done + chunk) * 2048)
+        sb = slice(done * tb, (done + chunk) * tb)
+        host = [x[sv].view(torch.int16).cpu().numpy().view(np.uint16) for x in xs]
+        t0 = time.perf_counter()
+        packed = [o.encode(bits, w.io_dtype, h) for h in host]
+        if w.reduce:
+            po, yo = o.reduce(bits, w.io_dtype, packed, chunk * 2048)
+        else:
+            po, yo = None, o.decode(bits, w.io_dtype, packed[0], chunk * 2048)
+        busy += time.perf_counter() - t0
+        if po is not None:
+            ok &= bool(np.array_equal(po, out[sb].cpu().numpy()))
+        ok &= bool(np.array_equal(yo, y[sv].view(torch.int16).cpu().numpy().view(np.uint16)))
+        done += chunk
+    gbs = w.ranks * done * 2048 * 2 / busy / 1e9
+    sample = (f"first {done} tiles ({done * 2048} values) of each of the {w.ranks} rank buffers of "
+              f"{w.name}: oracle encode x{w.ranks} + " + ("reduce with decode" if w.reduce else "decode")
+              + f", {busy:.1f} s of oracle time, one thread")
+    return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": sample}, ok
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the sharded "
+              "two-shot exchange is described, not built); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_quantized_all_amd as qa
+    import workloads as W
+
+    name = args.workload or W.BENCH_WORKLOAD
+    w = W.WORKLOADS[name]
+    qa.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    xs = W.inputs(w, seed=args.seed, device=dev)
+    pb = qa.qr_packed_bytes(w.fmt, w.n)
+    packed = [torch.empty(pb, dtype=torch.uint8, device=dev) for _ in range(w.ranks)]
+    out = torch.empty(pb, dtype=torch.uint8, device=dev) if w.reduce else None
+    y = torch.empty(w.n, dtype=w.dtype, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        for r in range(w.ranks):
+            if ev is not None:
+                ev["encode"][0].append(torch.cuda.Event(enable_timing=True))
+                ev["encode"][0][-1].record(stream)
+            qa.qr_encode(w.fmt, xs[r], packed[r], stream=stream)
+            if ev is not None:
+                ev["encode"][1].append(torch.cuda.Event(enable_timing=True))
+                ev["encode"][1][-1].record(stream)
+        kname = "reduce" if w.reduce else "decode"
+        if ev is not None:
+            ev[kname][0].append(torch.cuda.Event(enable_timing=True))
+            ev[kname][0][-1].record(stream)
+        if w.reduce:
+            qa.qr_reduce_compressed(w.fmt, w.dtype, packed, w.n, packed_out=out, y_out=y, stream=stream)
+        else:
+            qa.qr_decode(w.fmt, packed[0], w.n, w.dtype, y=y, stream=stream)
+        if ev is not None:
+            ev[kname][1].append(torch.cuda.Event(enable_timing=True))
+            ev[kname][1][-1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region 1: K clean steps between two events
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    # timed region 2: the same K steps with an event pair around every launch
+    ev = {"encode": ([], []), "reduce": ([], []), "decode": ([], [])}
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step(ev)
+    torch.cuda.synchronize()
+    kern_us = {}
+    for k, (a, b) in ev.items():
+        if a:
+            kern_us[k] = sum(x.elapsed_time(z) for x, z in zip(a, b)) / len(a) * 1e3
+    print(f"# {name}: {ms_per_step:.4f} ms/step; per-launch us: "
+          + ", ".join(f"{k}={v:.2f}" for k, v in kern_us.items()), file=sys.stderr, flush=True)
+
+    ab = algorithmic_bytes(w)
+    launches = {"encode": w.ranks, "reduce": 1 if w.reduce else 0, "decode": 0 if w.reduce else 1}
+    step_bytes = sum(ab[k] * launches[k] for k in launches)
+    fp16_input = w.ranks * w.n * 2
+    value = fp16_input / (ms_per_step * 1e-3) / 1e9
+    pipe_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    kernels = {}
+    for k, us in kern_us.items():
+        g = ab[k] / (us * 1e-6) / 1e9
+        kernels[k] = {"us_per_launch": round(us, 3), "launches_per_step": launches[k],
+                      "algorithmic_bytes": int(ab[k]), "achieved_gbs": round(g, 1),
+                      "frac": round(g / PEAK_HBM_GBS, 4)}
+    dom = max(kern_us, key=lambda k: kern_us[k] * launches[k])
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["achieved_gbs"],
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": kernels[dom]["frac"],
+                "traffic": traffic_from_profiles(dom)}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "format": w.fmt, "io_dtype": w.io_dtype, "ranks": w.ranks,
+                   "values_per_rank": w.n, "shape": list(w.shape), "seed": args.seed},
+        "pct_hbm_peak": round(100 * pipe_gbs / PEAK_HBM_GBS, 2),
+        "pipeline_hbm_gbs": round(pipe_gbs, 1),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        cb, ok = cpu_baseline(w, xs, out, y, args.cpu_seconds)
+        result["cpu_baseline"] = cb
+        result["parity_sample"] = ok
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

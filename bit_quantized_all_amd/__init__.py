@@ -1,0 +1,7 @@
+"""MI355X (gfx950) block-quantization codec and compressed-domain reduction.
+
+The kernels live in ``csrc/`` and are built into ``libqr.so``; ``qr`` is the
+ctypes binding of the C ABI declared in ``include/qr.h``.
+"""
+from .qr import (FORMATS, MAX_RANKS, QRError, TILE_VALUES, lib, qr_decode, qr_encode,  # noqa: F401
+                 qr_packed_bytes, qr_reduce_compressed, qr_status_string)

@@ -1,0 +1,314 @@
+// qr_codec.hpp -- gfx950 device code of the 32-value block codec.
+//
+// Format ("QuickReduce INT3 quantization and benchmarking on MI355", section
+// "Design Highlights"; INT8 extends the same block framework to 8 bits):
+//   block  = 32 consecutive values, one fp16 scale d = fp16(min(max|x|/Q, 65504))
+//   code   = clamp(round_half_even(x * e), -Q, Q-1) + Q, e = fp32(1/d) (0 if d == 0)
+//   INT4   word u = unit of 8 values, value j at bits 4j (lowest first, as the
+//          packed int32 nibbles of vLLM PR #54965 / PR #43389)
+//   INT3   2-bit plane (uint16 per unit, value j at bits 2j) + 1-bit plane
+//          (uint8 per unit, value j at bit j)
+//   decode = (code - Q) * d, exact in fp32.
+//
+// Work mapping: one lane owns one block (32 values), one 64-lane wave owns one
+// 2048-value tile.  The block maximum and the scale are computed once per
+// lane with no cross-lane traffic; the fp16/bf16 side of a tile is moved
+// through a wave-private LDS tile so that every global access is a coalesced
+// 16-byte access.  Nothing here is a contraction, so there is no MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qr {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTileValues = 2048;
+constexpr int kBlockValues = 32;
+constexpr int kWave = 64;
+constexpr int kChunks = kTileValues * 2 / 16;  // 16-byte chunks of one fp16/bf16 tile
+
+enum { kFp16 = 0, kBf16 = 1 };
+
+template <int BITS>
+struct Format;
+template <>
+struct Format<3> {
+  static constexpr int kQ = 4;
+  static constexpr int kTileBytes = 896;   // 512 (2-bit plane) + 256 (1-bit plane) + 128
+  static constexpr int kScaleOffset = 768;
+  static constexpr int kHighOffset = 512;  // the 1-bit plane
+  static constexpr int kShift = 5;         // decoded bytes hold 32 * k
+};
+template <>
+struct Format<4> {
+  static constexpr int kQ = 8;
+  static constexpr int kTileBytes = 1152;  // 1024 + 128
+  static constexpr int kScaleOffset = 1024;
+  static constexpr int kShift = 4;         // decoded bytes hold 16 * k
+};
+template <>
+struct Format<8> {
+  static constexpr int kQ = 128;
+  static constexpr int kTileBytes = 2176;  // 2048 + 128
+  static constexpr int kScaleOffset = 2048;
+  static constexpr int kShift = 0;
+};
+
+// Packed codes of one block as held by its lane.
+template <int BITS>
+struct Block;
+template <>
+struct Block<4> {
+  uint32_t w[4];  // units 0..3
+};
+template <>
+struct Block<3> {
+  uint32_t low[2];  // 2-bit plane: units 0,1 in low[0] (unit 0 in bits 0..15), units 2,3 in low[1]
+  uint32_t high;    // 1-bit plane: byte u = unit u
+};
+template <>
+struct Block<8> {
+  uint32_t w[8];  // byte i of the block = value i
+};
+
+// ---------------------------------------------------------------------------
+// dtype <-> fp32
+// ---------------------------------------------------------------------------
+
+template <int DT>
+__device__ __forceinline__ float lo_to_f32(uint32_t w) {
+  if constexpr (DT == kFp16)
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)w);
+  else
+    return __builtin_bit_cast(float, w << 16);
+}
+
+template <int DT>
+__device__ __forceinline__ float hi_to_f32(uint32_t w) {
+  if constexpr (DT == kFp16)
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  else
+    return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+// Two fp32 values to a packed dtype pair (low half first), round to nearest even.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  f32x2 v = {a, b};
+  if constexpr (DT == kFp16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// The dtype value nearest to s (ties to even), as fp32.
+template <int DT>
+__device__ __forceinline__ float round_to_dtype(float s) {
+  if constexpr (DT == kFp16)
+    return (float)(_Float16)s;
+  else
+    return (float)(__bf16)s;
+}
+
+// Signed byte i of x as fp32 (one SDWA conversion on gfx950).
+__device__ __forceinline__ float sbyte(uint32_t x, int i) { return (float)(int8_t)(x >> (8 * i)); }
+
+// ---------------------------------------------------------------------------
+// wave-private LDS tile: 256 chunks of 16 bytes, swizzled so that both the
+// row-order access (lane L, chunk L + 64k) and the block-order access (lane
+// l, chunks 4l..4l+3) hit 8 distinct 16-byte bank groups per 8 lanes.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int swz(int c) { return (c & ~7) | ((c + (c >> 3)) & 7); }
+
+// Makes one lane's LDS writes visible to the other lanes of its wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
+// packing of codes (code in the low byte of each word of c[])
+// ---------------------------------------------------------------------------
+
+// bytes [a.b0, b.b0, 0, 0] and [0, 0, a.b0, b.b0]
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+}
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x04000c0cu);
+}
+
+// INT4 word of one unit: value j at bits 4j.
+__device__ __forceinline__ uint32_t pack_int4_unit(const uint32_t* c) {
+  uint32_t even = lo_pair(c[0], c[2]) | hi_pair(c[4], c[6]);  // bytes c0 c2 c4 c6
+  uint32_t odd = lo_pair(c[1], c[3]) | hi_pair(c[5], c[7]);   // bytes c1 c3 c5 c7
+  return even | (odd << 4);
+}
+
+// INT8 word: bytes c0 c1 c2 c3.
+__device__ __forceinline__ uint32_t pack_int8_word(const uint32_t* c) {
+  return lo_pair(c[0], c[1]) | hi_pair(c[2], c[3]);
+}
+
+__device__ __forceinline__ uint32_t bit_select(uint32_t mask, uint32_t a, uint32_t b) {
+  return (a & mask) | (b & ~mask);  // v_bfi_b32
+}
+
+// INT3 planes of 16 values (two units): the 2-bit plane dword (unit 0 in the
+// low 16 bits) and a word whose bytes 0 and 2 are the two 1-bit plane bytes.
+__device__ __forceinline__ void pack_int3_pair(const uint32_t* c, uint32_t& low, uint32_t& highx) {
+  uint32_t g[4];  // g[r] byte b = code of value 4b + r
+#pragma unroll
+  for (int r = 0; r < 4; ++r) g[r] = lo_pair(c[r], c[4 + r]) | hi_pair(c[8 + r], c[12 + r]);
+  // byte b of `low` = low pairs of values 4b..4b+3 at bits 0,2,4,6
+  uint32_t y = bit_select(0xC0C0C0C0u, g[3] << 6, g[2] << 4);
+  y = bit_select(0xF0F0F0F0u, y, g[1] << 2);
+  low = bit_select(0xFCFCFCFCu, y, g[0]);
+  // byte b bits 0..3 of `s` = high bits of values 4b..4b+3
+  uint32_t s = (g[0] >> 2) & 0x01010101u;
+  s = bit_select(0x02020202u, g[1] >> 1, s);
+  s = bit_select(0x04040404u, g[2], s);
+  s = bit_select(0x08080808u, g[3] << 1, s);
+  highx = s | (s >> 4);
+}
+
+// ---------------------------------------------------------------------------
+// one block: encode (from exact dtype values in fp32) and decode
+// ---------------------------------------------------------------------------
+
+// Quantizes the 32 values z[] of one block.  Returns the fp16 scale bits; k[]
+// receives code - Q as fp32 (an exact small integer) for an immediate decode.
+template <int BITS>
+__device__ __forceinline__ uint32_t encode_block(const float (&z)[kBlockValues], Block<BITS>& blk,
+                                                 float (&k)[kBlockValues]) {
+  constexpr int Q = Format<BITS>::kQ;
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kBlockValues; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(z[i]));
+  // scale: m / Q is exact; saturate at the largest finite fp16, round to nearest even
+  const _Float16 dh = (_Float16)__builtin_fminf(m * (1.0f / Q), 65504.0f);
+  const float d = (float)dh;
+  const float e = (d == 0.0f) ? 0.0f : 1.0f / d;  // correctly rounded division
+  // q = clamp(rint(z*e), -Q, Q-1) + Q via 2^23 + Q: adding it rounds to an
+  // integer (half to even; Q is even) and leaves the code in the low bits.
+  constexpr float kMagic = 8388608.0f + Q;
+  uint32_t c[kBlockValues];
+#pragma unroll
+  for (int i = 0; i < kBlockValues; ++i) {
+    const float v = z[i] * e;
+    const float t = __builtin_amdgcn_fmed3f(v + kMagic, 8388608.0f, 8388608.0f + (2 * Q - 1));
+    c[i] = __builtin_bit_cast(uint32_t, t);
+    k[i] = t - kMagic;
+  }
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) blk.w[u] = pack_int4_unit(c + 8 * u);
+  } else if constexpr (BITS == 8) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) blk.w[w] = pack_int8_word(c + 4 * w);
+  } else {
+    uint32_t h0, h1;
+    pack_int3_pair(c, blk.low[0], h0);
+    pack_int3_pair(c + 16, blk.low[1], h1);
+    blk.high = __builtin_amdgcn_perm(h1, h0, 0x06040200u);
+  }
+  return __builtin_bit_cast(uint16_t, dh);
+}
+
+// Decodes one block into kk[i] = 2^Format::kShift * (code_i - Q) as fp32.
+// The value is kk[i] * (d * 2^-kShift), an exact product.
+template <int BITS>
+__device__ __forceinline__ void decode_block(const Block<BITS>& blk, float (&kk)[kBlockValues]) {
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t a = blk.w[u] ^ 0x88888888u;  // nibble = code - 8 in two's complement
+      const uint32_t hi = a & 0xF0F0F0F0u;        // odd values, 16 * k per byte
+      const uint32_t lo = (a << 4) & 0xF0F0F0F0u; // even values
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kk[8 * u + 2 * i] = sbyte(lo, i);
+        kk[8 * u + 2 * i + 1] = sbyte(hi, i);
+      }
+    }
+  } else if constexpr (BITS == 8) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t a = blk.w[w] ^ 0x80808080u;  // byte = code - 128
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kk[4 * w + i] = sbyte(a, i);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t low = blk.low[h];  // byte b: low pairs of values 16h + 4b + 0..3
+      // byte b bits 0..3: high bits of the same values, inverted (sign of k)
+      uint32_t x = (blk.high >> (16 * h)) & 0xffffu;
+      x = (x | (x << 8)) & 0x00FF00FFu;
+      x = (x | (x << 4)) & 0x0F0F0F0Fu;
+      const uint32_t nx = x ^ 0x0F0F0F0Fu;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // byte b = (low pair << 5) | (!high << 7) = 32 * (code - 4) as int8
+        const uint32_t l = (i < 3 ? (low << (5 - 2 * i)) : (low >> 1)) & 0x60606060u;
+        const uint32_t s = (nx << (7 - i)) & 0x80808080u;
+        const uint32_t b = l | s;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) kk[16 * h + 4 * bb + i] = sbyte(b, bb);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// global <-> lane block data
+// ---------------------------------------------------------------------------
+
+template <int BITS>
+__device__ __forceinline__ void load_block(const uint8_t* __restrict__ tile, int g, Block<BITS>& blk,
+                                           uint32_t& scale) {
+  if constexpr (BITS == 4) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + 16 * g));
+    blk.w[0] = v.x; blk.w[1] = v.y; blk.w[2] = v.z; blk.w[3] = v.w;
+  } else if constexpr (BITS == 8) {
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + 32 * g));
+    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + 32 * g + 16));
+    blk.w[0] = a.x; blk.w[1] = a.y; blk.w[2] = a.z; blk.w[3] = a.w;
+    blk.w[4] = b.x; blk.w[5] = b.y; blk.w[6] = b.z; blk.w[7] = b.w;
+  } else {
+    const u32x2 lw = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tile + 8 * g));
+    blk.low[0] = lw.x; blk.low[1] = lw.y;
+    blk.high = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(tile + Format<3>::kHighOffset + 4 * g));
+  }
+  scale = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(tile + Format<BITS>::kScaleOffset + 2 * g));
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_block(uint8_t* __restrict__ tile, int g, const Block<BITS>& blk,
+                                            uint32_t scale) {
+  if constexpr (BITS == 4) {
+    *reinterpret_cast<u32x4*>(tile + 16 * g) = u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]};
+  } else if constexpr (BITS == 8) {
+    *reinterpret_cast<u32x4*>(tile + 32 * g) = u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]};
+    *reinterpret_cast<u32x4*>(tile + 32 * g + 16) = u32x4{blk.w[4], blk.w[5], blk.w[6], blk.w[7]};
+  } else {
+    *reinterpret_cast<u32x2*>(tile + 8 * g) = u32x2{blk.low[0], blk.low[1]};
+    *reinterpret_cast<uint32_t*>(tile + Format<3>::kHighOffset + 4 * g) = blk.high;
+  }
+  *reinterpret_cast<uint16_t*>(tile + Format<BITS>::kScaleOffset + 2 * g) = (uint16_t)scale;
+}
+
+// fp32 of an fp16 scale held in the low 16 bits.
+__device__ __forceinline__ float scale_f32(uint32_t s) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)s);
+}
+
+}  // namespace qr

@@ -1,0 +1,122 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/qr.h declares, and rejects bad arguments before any HIP call (so these
+run without a GPU; no valid compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_all_amd as qa
+from bit_quantized_all_amd import qr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qr.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qr_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return qa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == {"qr_packed_bytes", "qr_encode", "qr_decode", "qr_reduce_compressed",
+                          "qr_status_string"}
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_packed_bytes(L):
+    assert L.qr_packed_bytes(3, 2048) == 896
+    assert L.qr_packed_bytes(4, 2048) == 1152
+    assert L.qr_packed_bytes(8, 2048) == 2176
+    assert L.qr_packed_bytes(4, 2048 * 65536) == 1152 * 65536
+    assert L.qr_packed_bytes(4, 0) == 0
+    for bad_n in (1, 2047, 2049, 4096 + 32):
+        assert L.qr_packed_bytes(4, bad_n) == 0
+    for bad_fmt in (0, 2, 5, 6, 16):
+        assert L.qr_packed_bytes(bad_fmt, 2048) == 0
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert L.qr_status_string(s) and L.qr_status_string(s) != b"unknown status"
+    assert L.qr_status_string(99) == b"unknown status"
+
+
+# Fake, never-dereferenced device addresses: every call below fails validation.
+A = 0x7f0000000000
+B = 0x7f0100000000
+C = 0x7f0200000000
+
+
+def enc(L, fmt=4, dt=0, x=A, p=B, n=2048):
+    return L.qr_encode(fmt, dt, x, p, n, None)
+
+
+def dec(L, fmt=4, dt=0, p=A, y=B, n=2048):
+    return L.qr_decode(fmt, dt, p, y, n, None)
+
+
+def red(L, fmt=4, dt=0, ranks=(A,), R=None, out=B, y=C, n=2048):
+    arr = (ctypes.c_void_p * max(1, len(ranks)))(*ranks) if ranks is not None else None
+    return L.qr_reduce_compressed(fmt, dt, arr, len(ranks) if R is None else R, out, y, n, None)
+
+
+def test_encode_validation(L):
+    assert enc(L, fmt=5) == qr.QR_ERR_UNSUPPORTED
+    assert enc(L, dt=2) == qr.QR_ERR_UNSUPPORTED
+    assert enc(L, n=2047) == qr.QR_ERR_SIZE
+    assert enc(L, n=4096 + 2) == qr.QR_ERR_SIZE
+    assert enc(L, x=0) == qr.QR_ERR_ARG
+    assert enc(L, p=0) == qr.QR_ERR_ARG
+    assert enc(L, x=A + 8) == qr.QR_ERR_ALIGN
+    assert enc(L, p=B + 2) == qr.QR_ERR_ALIGN
+    # packed starts inside x (x spans 2*n bytes), or x starts inside packed
+    assert enc(L, x=A, p=A + 4096 - 16) == qr.QR_ERR_ALIAS
+    assert enc(L, x=A + 1152 - 16, p=A) == qr.QR_ERR_ALIAS
+    # the empty call is valid and launches nothing, whatever the pointers
+    assert enc(L, n=0, x=0, p=0) == qr.QR_OK
+
+
+def test_decode_validation(L):
+    assert dec(L, fmt=0) == qr.QR_ERR_UNSUPPORTED
+    assert dec(L, dt=-1) == qr.QR_ERR_UNSUPPORTED
+    assert dec(L, n=100) == qr.QR_ERR_SIZE
+    assert dec(L, p=0) == qr.QR_ERR_ARG
+    assert dec(L, y=0) == qr.QR_ERR_ARG
+    assert dec(L, y=B + 4) == qr.QR_ERR_ALIGN
+    assert dec(L, p=A, y=A + 1024) == qr.QR_ERR_ALIAS
+    assert dec(L, n=0, p=0, y=0) == qr.QR_OK
+
+
+def test_reduce_validation(L):
+    assert red(L, fmt=7) == qr.QR_ERR_UNSUPPORTED
+    assert red(L, dt=3) == qr.QR_ERR_UNSUPPORTED
+    assert red(L, R=0) == qr.QR_ERR_ARG
+    assert red(L, ranks=[A] * 17) == qr.QR_ERR_ARG
+    assert red(L, n=2048 + 1) == qr.QR_ERR_SIZE
+    assert red(L, ranks=[A, 0]) == qr.QR_ERR_ARG
+    assert red(L, out=0) == qr.QR_ERR_ARG
+    assert L.qr_reduce_compressed(4, 0, None, 1, B, C, 2048, None) == qr.QR_ERR_ARG
+    # overlapping or repeated input ranks are allowed (not checked here: a valid call would launch)
+    assert red(L, ranks=[A, A + 8]) == qr.QR_ERR_ALIGN       # ... but must be aligned
+    assert red(L, out=B + 8) == qr.QR_ERR_ALIGN
+    assert red(L, y=C + 2) == qr.QR_ERR_ALIGN
+    assert red(L, ranks=[A, B - 512]) == qr.QR_ERR_ALIAS     # a rank overlaps packed_out
+    assert red(L, y=A + 1024) == qr.QR_ERR_ALIAS             # y_out overlaps a rank
+    assert red(L, out=C + 2048) == qr.QR_ERR_ALIAS           # outputs overlap each other
+    assert red(L, n=0, ranks=[0], out=0, y=0) == qr.QR_OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        qa.qr_encode("int4", torch.zeros(2048, dtype=torch.float16), torch.zeros(1152, dtype=torch.uint8))

@@ -1,0 +1,272 @@
+"""Parity of the HIP path with the CPU oracle (MI355X only).
+
+Every comparison is element by element on the same seeded inputs: packed
+codes and scales must be bit-identical, and decoded / reduced fp16/bf16
+outputs bit-identical as well (the acceptance bar allows 1 ulp of the output
+dtype for those; every step is a correctly rounded IEEE operation, so exact
+equality is what is expected and what is asserted).  Sizes span several
+tiles, waves and workgroups, with a ragged last workgroup; the full-size
+workloads are checked on sampled tiles, which the oracle computes one by one
+(tiles are independent), plus properties that hold at any size.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle_pins as P
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ("int3", "int4", "int8")
+BITS = {"int3": 3, "int4": 4, "int8": 8}
+DT = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def qa():
+    import bit_quantized_all_amd as qa
+    qa.lib()
+    assert torch.cuda.is_available()
+    return qa
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def u16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def dev(a, dtype=None):
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16).copy()).view(dtype)
+    else:
+        t = torch.from_numpy(a.copy())
+    return t.cuda()
+
+
+def gen(kind, dtype, n, seed):
+    """Host fp16/bf16 bit patterns for a named value family."""
+    rng = np.random.default_rng(seed)
+    nb = n // 32
+    if kind == "normal":
+        x = rng.standard_normal(n)
+    elif kind == "outliers":
+        x = rng.standard_normal(n)
+        x[rng.random(n) < 0.001] *= 50
+    elif kind == "scales":      # block scales spread over many binades, incl. fp16 subnormal scales
+        x = rng.standard_normal((nb, 32)) * np.exp(rng.uniform(-14, 9, size=(nb, 1)))
+    elif kind == "specials":    # zero blocks, -0, tiny, huge and exact multiples of a scale
+        x = rng.standard_normal((nb, 32))
+        sel = rng.integers(0, 6, nb)
+        x[sel == 0] = 0.0
+        x[sel == 1] = -0.0
+        x[sel == 2] *= 2.0 ** -20
+        x[sel == 3] = rng.integers(-8, 8, size=(int((sel == 3).sum()), 32)) * 0.25
+        x[sel == 4] *= 3000.0
+        x = x.ravel()
+    else:
+        raise ValueError(kind)
+    x = np.asarray(x, np.float64).ravel()
+    if dtype == "fp16":
+        return P.f16_bits(np.clip(x, -65504, 65504))
+    return P.bf16_bits(x.astype(np.float32).astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
+# encode / decode
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("ntiles", [1, 5, 37, 1031])
+@pytest.mark.parametrize("kind", ["normal", "outliers", "scales", "specials"])
+def test_encode_decode_parity(qa, oracle, fmt, dtype, ntiles, kind):
+    n = ntiles * 2048
+    xb = gen(kind, dtype, n, seed=ntiles * 7 + len(kind))
+    log(f"encode/decode {fmt} {dtype} tiles={ntiles} {kind}")
+    x = dev(xb, DT[dtype])
+    p = qa.qr_encode(fmt, x)
+    y = qa.qr_decode(fmt, p, n, DT[dtype])
+    torch.cuda.synchronize()
+    want_p = oracle.encode(BITS[fmt], dtype, xb)
+    got_p = p.cpu().numpy()
+    if not np.array_equal(got_p, want_p):
+        gc, gs = P.unpack(BITS[fmt], got_p)
+        wc, ws = P.unpack(BITS[fmt], want_p)
+        bad = np.argwhere(gc != wc)
+        raise AssertionError(f"codes differ at {bad[:5].tolist()} (scales equal: {np.array_equal(gs, ws)})")
+    want_y = oracle.decode(BITS[fmt], dtype, want_p, n)
+    assert np.array_equal(u16(y), want_y)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_decode_arbitrary_packed(qa, oracle, fmt, dtype):
+    """Decode of packed data that no encoder produced: every code, every
+    finite fp16 scale (normal, subnormal, zero)."""
+    bits = BITS[fmt]
+    rng = np.random.default_rng(bits)
+    T = 517
+    codes = rng.integers(0, 1 << bits, size=(T, 2048))
+    sb = rng.integers(0, 0x7C00, size=(T, 64)).astype(np.uint16)
+    sb[:, :3] = [0, 1, 0x7BFF]
+    packed = P.pack(bits, codes, sb)
+    log(f"decode arbitrary {fmt} {dtype}")
+    y = qa.qr_decode(fmt, dev(packed), T * 2048, DT[dtype])
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(y), oracle.decode(bits, dtype, packed, T * 2048))
+
+
+# ---------------------------------------------------------------------------
+# fused reduction
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8, 11, 16])
+@pytest.mark.parametrize("ntiles", [3, 133])
+def test_reduce_parity(qa, oracle, fmt, dtype, R, ntiles):
+    bits = BITS[fmt]
+    n = ntiles * 2048
+    kinds = ["normal", "outliers", "scales", "specials"]
+    xs = [gen(kinds[r % 4], dtype, n, seed=1000 * R + 10 * r + ntiles) for r in range(R)]
+    log(f"reduce {fmt} {dtype} R={R} tiles={ntiles}")
+    packed = [qa.qr_encode(fmt, dev(x, DT[dtype])) for x in xs]
+    out, y = qa.qr_reduce_compressed(fmt, DT[dtype], packed, n)
+    out2, none = qa.qr_reduce_compressed(fmt, DT[dtype], packed, n, with_output=False)
+    torch.cuda.synchronize()
+    assert none is None
+    wranks = [oracle.encode(bits, dtype, x) for x in xs]
+    for r in range(R):
+        assert np.array_equal(packed[r].cpu().numpy(), wranks[r]), r
+    wout, wy = oracle.reduce(bits, dtype, wranks, n)
+    got = out.cpu().numpy()
+    if not np.array_equal(got, wout):
+        gc, gs = P.unpack(bits, got)
+        wc, ws = P.unpack(bits, wout)
+        raise AssertionError(f"re-encoded tile differs: codes at {np.argwhere(gc != wc)[:5].tolist()}, "
+                             f"scales at {np.argwhere(gs != ws)[:5].tolist()}")
+    assert np.array_equal(u16(y), wy)
+    assert np.array_equal(out2.cpu().numpy(), wout)
+
+
+def test_reduce_repeated_rank_buffer(qa, oracle):
+    """The same buffer passed for several ranks (inputs may alias each other)."""
+    n = 9 * 2048
+    xb = gen("normal", "fp16", n, 3)
+    p = qa.qr_encode("int4", dev(xb, torch.float16))
+    out, y = qa.qr_reduce_compressed("int4", torch.float16, [p, p, p], n)
+    torch.cuda.synchronize()
+    wp = oracle.encode(4, "fp16", xb)
+    wout, wy = oracle.reduce(4, "fp16", [wp, wp, wp], n)
+    assert np.array_equal(out.cpu().numpy(), wout) and np.array_equal(u16(y), wy)
+
+
+def test_reduce_fp16_overflow(qa, oracle):
+    """An fp16 sum above 65504 rounds to inf; the re-encode saturates the scale
+    at 65504 and the codes at the ends of the range, on both sides."""
+    n = 2 * 2048
+    xb = [P.f16_bits(np.full(n, 60000.0 * (1 if r % 2 == 0 else 1))) for r in range(4)]
+    xb[1][::3] = P.f16_bits(-60000.0)
+    log("reduce fp16 overflow")
+    packed = [qa.qr_encode("int4", dev(x, torch.float16)) for x in xb]
+    out, y = qa.qr_reduce_compressed("int4", torch.float16, packed, n)
+    torch.cuda.synchronize()
+    wout, wy = oracle.reduce(4, "fp16", [oracle.encode(4, "fp16", x) for x in xb], n)
+    assert np.array_equal(out.cpu().numpy(), wout) and np.array_equal(u16(y), wy)
+
+
+def test_golden_rank_order_on_gpu(qa):
+    """The hand-derived rank-order example (tests/golden/reduce_rank_order.txt)."""
+    scale, elems = P._golden_expect("reduce_rank_order.txt")
+    vals = np.zeros((4, 2048))
+    vals[0, [0, 2, 3]] = [-16, 2, 14]
+    vals[1, [0, 1]] = [-2.0 ** -20, -2.0 ** -17]
+    vals[2, [0, 2, 3]] = [14, -16, 2]
+    vals[3, [0, 2, 3]] = [2, 14, -16]
+    packed = [qa.qr_encode("int4", dev(P.f16_bits(v), torch.float16)) for v in vals]
+    out, y = qa.qr_reduce_compressed("int4", torch.float16, packed, 2048)
+    torch.cuda.synchronize()
+    codes, sb = P.unpack(4, out.cpu().numpy())
+    yb = u16(y)
+    assert sb[0, 0] == scale
+    for name, idx in (("A", 0), ("B", 1), ("E2", 2), ("E3", 3)):
+        assert codes[0, idx] == elems[name][0] and yb[idx] == elems[name][1], name
+
+
+# ---------------------------------------------------------------------------
+# the workloads, at CPU-checkable size and at full size (sampled tiles)
+# ---------------------------------------------------------------------------
+
+def run_pipeline(qa, w, xs):
+    packed = [qa.qr_encode(w.fmt, x) for x in xs]
+    if not w.reduce:
+        return packed, None, qa.qr_decode(w.fmt, packed[0], w.n, w.dtype)
+    out, y = qa.qr_reduce_compressed(w.fmt, w.dtype, packed, w.n)
+    return packed, out, y
+
+
+def check_tiles(oracle, w, xs_host_tiles, packed, out, y, tiles):
+    """Oracle on the given tiles of every rank vs the GPU's bytes there."""
+    bits = BITS[w.fmt]
+    tb = P.tile_bytes(bits)
+    idx_b = np.concatenate([np.arange(t * tb, (t + 1) * tb) for t in tiles])
+    idx_v = np.concatenate([np.arange(t * 2048, (t + 1) * 2048) for t in tiles])
+    nt = len(tiles) * 2048
+    wr = [oracle.encode(bits, w.io_dtype, xt) for xt in xs_host_tiles]
+    for r in range(len(wr)):
+        assert np.array_equal(packed[r][idx_b], wr[r]), f"rank {r} encode differs"
+    if out is None:
+        assert np.array_equal(y[idx_v], oracle.decode(bits, w.io_dtype, wr[0], nt))
+        return
+    wout, wy = oracle.reduce(bits, w.io_dtype, wr, nt)
+    assert np.array_equal(out[idx_b], wout), "re-encoded sum differs"
+    assert np.array_equal(y[idx_v], wy), "decoded sum differs"
+
+
+def test_smallest_workload_exact(qa, oracle):
+    """configs[0]-sized workload, every value."""
+    w = W.WORKLOADS["int3_r2_fp16_8k"]
+    xs = W.inputs(w, seed=0)
+    log("workload int3_r2_fp16_8k")
+    packed, out, y = run_pipeline(qa, w, [x.cuda() for x in xs])
+    torch.cuda.synchronize()
+    check_tiles(oracle, w, [u16(x) for x in xs], [p.cpu().numpy() for p in packed],
+                out.cpu().numpy(), u16(y), list(range(w.n // 2048)))
+
+
+@pytest.mark.parametrize("name", [k for k in W.WORKLOADS if k != "int3_r2_fp16_8k"])
+def test_workload_full_size_sampled(qa, oracle, name):
+    w = W.WORKLOADS[name]
+    log(f"workload {name} n={w.n} R={w.ranks}")
+    xs = W.inputs(w, seed=0, device="cuda")
+    packed, out, y = run_pipeline(qa, w, xs)
+    # a second run must give identical bytes (determinism)
+    packed2, out2, y2 = run_pipeline(qa, w, xs)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(packed, packed2))
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    if out is not None:
+        assert torch.equal(out, out2)
+        # the fused final decode equals the standalone decode of the re-encoded sum
+        yd = qa.qr_decode(w.fmt, out, w.n, w.dtype)
+        assert torch.equal(y.view(torch.int16), yd.view(torch.int16))
+    ntiles = w.n // 2048
+    rng = np.random.default_rng(ntiles)
+    tiles = sorted(set([0, 1, ntiles - 1, ntiles // 2] + list(rng.integers(0, ntiles, 60))))
+    tb = P.tile_bytes(BITS[w.fmt])
+    sel_v = torch.tensor(np.concatenate([np.arange(t * 2048, (t + 1) * 2048) for t in tiles]), device="cuda")
+    sel_b = np.concatenate([np.arange(t * tb, (t + 1) * tb) for t in tiles])
+    xs_t = [u16(x[sel_v]) for x in xs]
+    packed_full = [p.cpu().numpy() for p in packed]
+    y_host = np.zeros(w.n, np.uint16)
+    y_host[sel_v.cpu().numpy()] = u16(y[sel_v])
+    out_host = out.cpu().numpy() if out is not None else None
+    del sel_b
+    check_tiles(oracle, w, xs_t, packed_full, out_host, y_host, tiles)
