@@ -61,6 +61,54 @@ def traffic_from_profiles(kernel):
     return d.get("bytes_per_launch", {}).get(kernel)
 
 
+KERNEL_KEYS = {"encode": "encode_kernel", "reduce": "reduce_kernel", "decode": "decode_kernel"}
+COPY_KEY = "copy_kernel"   # torch's device copy kernel (the calibration copy of --copy-ref)
+
+
+def ingest_pmc(fetch_csv, write_csv, workload):
+    """HBM bytes per launch of each kernel from two rocprofv3 counter runs
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of
+    `bench.py --copy-ref --workload W`, each scaled so that the calibration copy
+    (n * 2 bytes read, n * 2 written) reads as its known size.  Written to
+    profiles/hbm_traffic.json with the hash of the kernel sources."""
+    import csv
+    import statistics
+
+    import workloads as W
+
+    w = W.WORKLOADS[workload]
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = row["Kernel_Name"]
+                key = next((k for k, v in KERNEL_KEYS.items() if v in name), None)
+                if key is None and "copy" in name.lower():
+                    key = "copy"
+                if key:
+                    vals.setdefault(key, []).append(float(row["Counter_Value"]))
+        return {k: statistics.median(v) for k, v in vals.items()}
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    known = w.n * 2
+    f_scale = known / (fetch["copy"] * 1024)
+    w_scale = known / (write["copy"] * 1024)
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "fetch_kib_per_launch": fetch, "write_kib_per_launch": write,
+           "bytes_per_launch": {k: round(fetch[k] * 1024 * f_scale + write[k] * 1024 * w_scale)
+                                for k in fetch if k in write and k != "copy"},
+           "algorithmic_bytes_per_launch": {k: int(v) for k, v in algorithmic_bytes(w).items()}}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(w, xs, out, y, seconds):
     """The oracle (single-threaded C) on consecutive tiles of every rank, from
     the first, until about `seconds` of oracle time; each chunk's inputs are
@@ -110,7 +158,17 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="also time a plain device copy of one rank's input (bandwidth reference and "
+                         "calibration kernel for the HBM traffic counters)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+
+    if args.ingest_pmc:
+        import workloads as W
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload or W.BENCH_WORKLOAD)
+        return
 
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the sharded "
@@ -136,26 +194,19 @@ def main():
     y = torch.empty(w.n, dtype=w.dtype, device=dev)
     torch.cuda.synchronize()
 
-    def step(ev=None):
-        for r in range(w.ranks):
-            if ev is not None:
-                ev["encode"][0].append(torch.cuda.Event(enable_timing=True))
-                ev["encode"][0][-1].record(stream)
-            qa.qr_encode(w.fmt, xs[r], packed[r], stream=stream)
-            if ev is not None:
-                ev["encode"][1].append(torch.cuda.Event(enable_timing=True))
-                ev["encode"][1][-1].record(stream)
-        kname = "reduce" if w.reduce else "decode"
-        if ev is not None:
-            ev[kname][0].append(torch.cuda.Event(enable_timing=True))
-            ev[kname][0][-1].record(stream)
+    def encode(r):
+        qa.qr_encode(w.fmt, xs[r], packed[r], stream=stream)
+
+    def finish():
         if w.reduce:
             qa.qr_reduce_compressed(w.fmt, w.dtype, packed, w.n, packed_out=out, y_out=y, stream=stream)
         else:
             qa.qr_decode(w.fmt, packed[0], w.n, w.dtype, y=y, stream=stream)
-        if ev is not None:
-            ev[kname][1].append(torch.cuda.Event(enable_timing=True))
-            ev[kname][1][-1].record(stream)
+
+    def step():
+        for r in range(w.ranks):
+            encode(r)
+        finish()
 
     for _ in range(args.warmup):
         step()
@@ -171,18 +222,40 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
 
-    # timed region 2: the same K steps with an event pair around every launch
-    ev = {"encode": ([], []), "reduce": ([], []), "decode": ([], [])}
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        step(ev)
-    torch.cuda.synchronize()
-    kern_us = {}
-    for k, (a, b) in ev.items():
-        if a:
-            kern_us[k] = sum(x.elapsed_time(z) for x, z in zip(a, b)) / len(a) * 1e3
+    # timed region 2: each kernel alone, K steps' worth of back-to-back launches
+    # between two events on the launch stream -> average launch duration
+    def timed(fn, launches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / launches * 1e3
+
+    kname = "reduce" if w.reduce else "decode"
+    kern_us = {
+        "encode": timed(lambda: [encode(r) for _ in range(args.steps) for r in range(w.ranks)],
+                        args.steps * w.ranks),
+        kname: timed(lambda: [finish() for _ in range(args.steps)], args.steps),
+    }
     print(f"# {name}: {ms_per_step:.4f} ms/step; per-launch us: "
           + ", ".join(f"{k}={v:.2f}" for k, v in kern_us.items()), file=sys.stderr, flush=True)
+
+    copy_ref = None
+    if args.copy_ref:
+        src, dst = xs[0], torch.empty_like(xs[0])
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        us = c0.elapsed_time(c1) / args.steps * 1e3
+        copy_ref = {"bytes": 4 * w.n, "us_per_launch": round(us, 3), "gbs": round(4 * w.n / us / 1e3, 1)}
+        del dst
 
     ab = algorithmic_bytes(w)
     launches = {"encode": w.ranks, "reduce": 1 if w.reduce else 0, "decode": 0 if w.reduce else 1}
@@ -221,6 +294,8 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if copy_ref:
+        result["copy_ref"] = copy_ref
     if not args.no_cpu_baseline:
         cb, ok = cpu_baseline(w, xs, out, y, args.cpu_seconds)
         result["cpu_baseline"] = cb

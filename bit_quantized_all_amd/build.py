@@ -24,10 +24,10 @@ FLAGS = [
 ]
 
 
-def build(out=LIB, extra=(), quiet=True):
+def build(out=LIB, extra=(), quiet=True, src=SRC):
     """Compile the kernels and the C ABI into ``out``; returns ``out``."""
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, SRC]
+    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, src]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"HIP build failed: {' '.join(cmd)}\n{res.stderr}")
@@ -35,6 +35,15 @@ def build(out=LIB, extra=(), quiet=True):
         sys.stderr.write(res.stderr)
     os.replace(tmp, out)
     return out
+
+
+TEST_HELPER_SRC = os.path.join(ROOT, "tests", "gpu_helpers", "scale_check.hip")
+TEST_HELPER_LIB = os.path.join(ROOT, "tests", "gpu_helpers", "libscale_check.so")
+
+
+def build_test_helpers(quiet=True):
+    """Test-only HIP helper that exercises the codec's device functions directly."""
+    return build(out=TEST_HELPER_LIB, src=TEST_HELPER_SRC, quiet=quiet)
 
 
 if __name__ == "__main__":

@@ -116,16 +116,41 @@ __device__ __forceinline__ float round_to_dtype(float s) {
     return (float)(__bf16)s;
 }
 
+// RN32(dtype_RNE(s) * e) for two values at once: one packed conversion to the
+// dtype, then for fp16 a mixed-precision FMA that reads the fp16 halves
+// directly (fma(z, e, +0) rounds z*e once; the sign of a zero product does
+// not matter to the quantizer).
+template <int DT>
+__device__ __forceinline__ void round_scale2(float s0, float s1, float e, float& v0, float& v1) {
+  f32x2 s = {s0, s1};
+  if constexpr (DT == kFp16) {
+    const f16x2 h = __builtin_convertvector(s, f16x2);
+    v0 = __builtin_fmaf((float)h.x, e, 0.0f);
+    v1 = __builtin_fmaf((float)h.y, e, 0.0f);
+  } else {
+    const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_convertvector(s, bf16x2));
+    v0 = __builtin_bit_cast(float, b << 16) * e;
+    v1 = __builtin_bit_cast(float, b & 0xffff0000u) * e;
+  }
+}
+
 // Signed byte i of x as fp32 (one SDWA conversion on gfx950).
 __device__ __forceinline__ float sbyte(uint32_t x, int i) { return (float)(int8_t)(x >> (8 * i)); }
 
 // ---------------------------------------------------------------------------
-// wave-private LDS tile: 256 chunks of 16 bytes, swizzled so that both the
-// row-order access (lane L, chunk L + 64k) and the block-order access (lane
-// l, chunks 4l..4l+3) hit 8 distinct 16-byte bank groups per 8 lanes.
+// wave-private LDS tile: 256 chunks of 16 bytes.  Chunk c lives in slot
+// c ^ t(c), an XOR swizzle of its low three bits by bits 2..5 chosen so that
+// both the row-order access (lane L, chunk L + 64k) and the block-order access
+// (lane l, chunks 4l + j) hit distinct 16-byte bank groups within every 8 and
+// every 16 consecutive lanes (no bank conflicts for 32- or 64-bank LDS).
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ int swz(int c) { return (c & ~7) | ((c + (c >> 3)) & 7); }
+__device__ __forceinline__ int swz(int c) { return c ^ (((c >> 2) & 5) | (((c >> 2) ^ (c >> 4)) & 2)); }
+// The chunk whose swizzled slot is s.
+__device__ __forceinline__ int unswz(int s) {
+  const int c2 = ((s >> 2) ^ (s >> 4)) & 1;
+  return s ^ (c2 | ((((s >> 3) ^ (s >> 5)) & 1) << 1) | (((s >> 4) & 1) << 2));
+}
 
 // Makes one lane's LDS writes visible to the other lanes of its wave.
 __device__ __forceinline__ void wave_lds_sync() {
@@ -184,43 +209,83 @@ __device__ __forceinline__ void pack_int3_pair(const uint32_t* c, uint32_t& low,
 // one block: encode (from exact dtype values in fp32) and decode
 // ---------------------------------------------------------------------------
 
-// Quantizes the 32 values z[] of one block.  Returns the fp16 scale bits; k[]
-// receives code - Q as fp32 (an exact small integer) for an immediate decode.
+// Magic constant 2^23 + Q: adding it to a value in [-Q, Q) rounds that value
+// to an integer (half to even, since Q is even) and leaves the biased code in
+// the low mantissa bits: bits(2^23 + Q + k) = 0x4B000000 + (k + Q).
 template <int BITS>
-__device__ __forceinline__ uint32_t encode_block(const float (&z)[kBlockValues], Block<BITS>& blk,
-                                                 float (&k)[kBlockValues]) {
+__device__ __forceinline__ constexpr float magic() {
+  return 8388608.0f + Format<BITS>::kQ;
+}
+
+// fp32(1 / d), correctly rounded, for d a positive finite fp16 value: the
+// hardware reciprocal estimate followed by one Newton step r + r * (1 - d * r)
+// (both FMAs single-rounded).  Exhaustively equal to the IEEE quotient 1.0f / d
+// over all 31743 positive finite fp16 values on gfx950 (the estimate alone is
+// off by an ulp for 2746 of them); three instructions instead of the eleven of
+// the general correctly rounded division.
+__device__ __forceinline__ float recip_fp16_value(float d) {
+  const float r = __builtin_amdgcn_rcpf(d);
+  return __builtin_fmaf(r, __builtin_fmaf(-d, r, 1.0f), r);
+}
+
+// Scale of a block from its absolute maximum m: d = fp16(min(m / Q, 65504))
+// (m / Q is exact).  Returns the fp16 bits; d and the encode multiplier
+// e = fp32(1 / d) (0 when d == 0) are set.
+template <int BITS>
+__device__ __forceinline__ uint32_t block_scale(float m, float& d, float& e) {
   constexpr int Q = Format<BITS>::kQ;
+  const _Float16 dh = (_Float16)__builtin_fminf(m * (1.0f / Q), 65504.0f);
+  d = (float)dh;
+  e = (d == 0.0f) ? 0.0f : recip_fp16_value(d);
+  return __builtin_bit_cast(uint16_t, dh);
+}
+
+// Code of one value: q = clamp(rint(RN32(x * e)), -Q, Q-1) + Q, returned as
+// the bits of 2^23 + q (low byte = q).  Clamping after the magic add equals
+// clamping before rounding because the bounds are integers.
+template <int BITS>
+__device__ __forceinline__ uint32_t quantize(float v) {
+  constexpr int Q = Format<BITS>::kQ;
+  const float t = __builtin_amdgcn_fmed3f(v + magic<BITS>(), 8388608.0f, 8388608.0f + (2 * Q - 1));
+  return __builtin_bit_cast(uint32_t, t);
+}
+
+// code - Q as fp32 from quantize()'s result (exact).
+template <int BITS>
+__device__ __forceinline__ float code_value(uint32_t t) {
+  return __builtin_bit_cast(float, t) - magic<BITS>();
+}
+
+// Packs 32 codes (low byte of each t[i]) into the lane's block.
+template <int BITS>
+__device__ __forceinline__ void pack_block(const uint32_t (&t)[kBlockValues], Block<BITS>& blk) {
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) blk.w[u] = pack_int4_unit(t + 8 * u);
+  } else if constexpr (BITS == 8) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) blk.w[w] = pack_int8_word(t + 4 * w);
+  } else {
+    uint32_t h0, h1;
+    pack_int3_pair(t, blk.low[0], h0);
+    pack_int3_pair(t + 16, blk.low[1], h1);
+    blk.high = __builtin_amdgcn_perm(h1, h0, 0x06040200u);
+  }
+}
+
+// Quantizes the 32 exact dtype values z[] of one block into t[] (see
+// quantize()); returns the fp16 scale bits and sets the decode scale d.
+template <int BITS>
+__device__ __forceinline__ uint32_t quantize_block(const float (&z)[kBlockValues], uint32_t (&t)[kBlockValues],
+                                                   float& d) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < kBlockValues; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(z[i]));
-  // scale: m / Q is exact; saturate at the largest finite fp16, round to nearest even
-  const _Float16 dh = (_Float16)__builtin_fminf(m * (1.0f / Q), 65504.0f);
-  const float d = (float)dh;
-  const float e = (d == 0.0f) ? 0.0f : 1.0f / d;  // correctly rounded division
-  // q = clamp(rint(z*e), -Q, Q-1) + Q via 2^23 + Q: adding it rounds to an
-  // integer (half to even; Q is even) and leaves the code in the low bits.
-  constexpr float kMagic = 8388608.0f + Q;
-  uint32_t c[kBlockValues];
+  float e;
+  const uint32_t bits = block_scale<BITS>(m, d, e);
 #pragma unroll
-  for (int i = 0; i < kBlockValues; ++i) {
-    const float v = z[i] * e;
-    const float t = __builtin_amdgcn_fmed3f(v + kMagic, 8388608.0f, 8388608.0f + (2 * Q - 1));
-    c[i] = __builtin_bit_cast(uint32_t, t);
-    k[i] = t - kMagic;
-  }
-  if constexpr (BITS == 4) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) blk.w[u] = pack_int4_unit(c + 8 * u);
-  } else if constexpr (BITS == 8) {
-#pragma unroll
-    for (int w = 0; w < 8; ++w) blk.w[w] = pack_int8_word(c + 4 * w);
-  } else {
-    uint32_t h0, h1;
-    pack_int3_pair(c, blk.low[0], h0);
-    pack_int3_pair(c + 16, blk.low[1], h1);
-    blk.high = __builtin_amdgcn_perm(h1, h0, 0x06040200u);
-  }
-  return __builtin_bit_cast(uint16_t, dh);
+  for (int i = 0; i < kBlockValues; ++i) t[i] = quantize<BITS>(z[i] * e);
+  return bits;
 }
 
 // Decodes one block into kk[i] = 2^Format::kShift * (code_i - Q) as fp32.
@@ -230,9 +295,9 @@ __device__ __forceinline__ void decode_block(const Block<BITS>& blk, float (&kk)
   if constexpr (BITS == 4) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint32_t a = blk.w[u] ^ 0x88888888u;  // nibble = code - 8 in two's complement
-      const uint32_t hi = a & 0xF0F0F0F0u;        // odd values, 16 * k per byte
-      const uint32_t lo = (a << 4) & 0xF0F0F0F0u; // even values
+      // high nibble of each byte, top bit flipped: 16 * (code - 8) as int8
+      const uint32_t hi = (blk.w[u] & 0xF0F0F0F0u) ^ 0x80808080u;         // odd values
+      const uint32_t lo = ((blk.w[u] << 4) & 0xF0F0F0F0u) ^ 0x80808080u;  // even values
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         kk[8 * u + 2 * i] = sbyte(lo, i);
@@ -272,38 +337,56 @@ __device__ __forceinline__ void decode_block(const Block<BITS>& blk, float (&kk)
 // global <-> lane block data
 // ---------------------------------------------------------------------------
 
-template <int BITS>
+// Global loads and stores with an optional non-temporal hint (for data that
+// is streamed through once and should not displace other cache lines).
+template <bool NT, typename T>
+__device__ __forceinline__ T ld(const T* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
+template <bool NT, typename T>
+__device__ __forceinline__ void st(T v, T* p) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+
+template <int BITS, bool NT>
 __device__ __forceinline__ void load_block(const uint8_t* __restrict__ tile, int g, Block<BITS>& blk,
                                            uint32_t& scale) {
   if constexpr (BITS == 4) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + 16 * g));
+    const u32x4 v = ld<NT>(reinterpret_cast<const u32x4*>(tile + 16 * g));
     blk.w[0] = v.x; blk.w[1] = v.y; blk.w[2] = v.z; blk.w[3] = v.w;
   } else if constexpr (BITS == 8) {
-    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + 32 * g));
-    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + 32 * g + 16));
+    const u32x4 a = ld<NT>(reinterpret_cast<const u32x4*>(tile + 32 * g));
+    const u32x4 b = ld<NT>(reinterpret_cast<const u32x4*>(tile + 32 * g + 16));
     blk.w[0] = a.x; blk.w[1] = a.y; blk.w[2] = a.z; blk.w[3] = a.w;
     blk.w[4] = b.x; blk.w[5] = b.y; blk.w[6] = b.z; blk.w[7] = b.w;
   } else {
-    const u32x2 lw = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tile + 8 * g));
+    const u32x2 lw = ld<NT>(reinterpret_cast<const u32x2*>(tile + 8 * g));
     blk.low[0] = lw.x; blk.low[1] = lw.y;
-    blk.high = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(tile + Format<3>::kHighOffset + 4 * g));
+    blk.high = ld<NT>(reinterpret_cast<const uint32_t*>(tile + Format<3>::kHighOffset + 4 * g));
   }
-  scale = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(tile + Format<BITS>::kScaleOffset + 2 * g));
+  scale = ld<NT>(reinterpret_cast<const uint16_t*>(tile + Format<BITS>::kScaleOffset + 2 * g));
 }
 
-template <int BITS>
+template <int BITS, bool NT>
 __device__ __forceinline__ void store_block(uint8_t* __restrict__ tile, int g, const Block<BITS>& blk,
                                             uint32_t scale) {
   if constexpr (BITS == 4) {
-    *reinterpret_cast<u32x4*>(tile + 16 * g) = u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]};
+    st<NT>(u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]}, reinterpret_cast<u32x4*>(tile + 16 * g));
   } else if constexpr (BITS == 8) {
-    *reinterpret_cast<u32x4*>(tile + 32 * g) = u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]};
-    *reinterpret_cast<u32x4*>(tile + 32 * g + 16) = u32x4{blk.w[4], blk.w[5], blk.w[6], blk.w[7]};
+    st<NT>(u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]}, reinterpret_cast<u32x4*>(tile + 32 * g));
+    st<NT>(u32x4{blk.w[4], blk.w[5], blk.w[6], blk.w[7]}, reinterpret_cast<u32x4*>(tile + 32 * g + 16));
   } else {
-    *reinterpret_cast<u32x2*>(tile + 8 * g) = u32x2{blk.low[0], blk.low[1]};
-    *reinterpret_cast<uint32_t*>(tile + Format<3>::kHighOffset + 4 * g) = blk.high;
+    st<NT>(u32x2{blk.low[0], blk.low[1]}, reinterpret_cast<u32x2*>(tile + 8 * g));
+    st<NT>(blk.high, reinterpret_cast<uint32_t*>(tile + Format<3>::kHighOffset + 4 * g));
   }
-  *reinterpret_cast<uint16_t*>(tile + Format<BITS>::kScaleOffset + 2 * g) = (uint16_t)scale;
+  st<NT>((uint16_t)scale, reinterpret_cast<uint16_t*>(tile + Format<BITS>::kScaleOffset + 2 * g));
 }
 
 // fp32 of an fp16 scale held in the low 16 bits.

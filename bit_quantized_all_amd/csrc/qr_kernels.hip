@@ -20,9 +20,44 @@
 
 namespace qr {
 
-constexpr int kWavesPerGroup = 4;
+// Launch shape: waves (tiles in flight) per workgroup and the grid cap above
+// which waves loop over further tiles (grid-stride).
+#ifndef QR_WAVES_PER_GROUP
+#define QR_WAVES_PER_GROUP 4
+#endif
+#ifndef QR_MAX_GROUPS
+#define QR_MAX_GROUPS (1 << 20)
+#endif
+// Non-temporal hints per kernel and direction (1 = streamed, 0 = cached).
+#ifndef QR_ENC_NT_LOAD
+#define QR_ENC_NT_LOAD 1
+#endif
+#ifndef QR_ENC_NT_STORE
+#define QR_ENC_NT_STORE 1
+#endif
+#ifndef QR_DEC_NT_LOAD
+#define QR_DEC_NT_LOAD 0
+#endif
+#ifndef QR_DEC_NT_STORE
+#define QR_DEC_NT_STORE 1
+#endif
+#ifndef QR_RED_NT_LOAD
+#define QR_RED_NT_LOAD 1
+#endif
+#ifndef QR_RED_NT_STORE
+#define QR_RED_NT_STORE 1
+#endif
+// 1: encode loads its fp16/bf16 tile straight into LDS (global_load_lds_dwordx4).
+#ifndef QR_ENC_LDS_DMA
+#define QR_ENC_LDS_DMA 0
+#endif
+// 1: issue every rank's loads before decoding; 0: let the scheduler pipeline them.
+#ifndef QR_RED_LOADS_FIRST
+#define QR_RED_LOADS_FIRST 1
+#endif
+constexpr int kWavesPerGroup = QR_WAVES_PER_GROUP;
 constexpr int kThreads = kWave * kWavesPerGroup;
-constexpr int kMaxGroups = 8192;
+constexpr int kMaxGroups = QR_MAX_GROUPS;
 
 // ---------------------------------------------------------------------------
 // encode
@@ -33,15 +68,26 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restr
                                                           uint8_t* __restrict__ packed, int ntiles) {
   __shared__ u32x4 lds[kWavesPerGroup][kChunks];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
   u32x4* tl = lds[wave];
   for (int tile = blockIdx.x * kWavesPerGroup + wave; tile < ntiles; tile += gridDim.x * kWavesPerGroup) {
     const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)tile * (kTileValues * 2));
+#if QR_ENC_LDS_DMA
+    // global -> LDS without VGPRs: instruction k writes slot 64k + lane, so lane
+    // fetches the chunk that the swizzle maps there (still one 1 KB span).
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      __builtin_amdgcn_global_load_lds(src + unswz(kWave * k + lane),
+                                       (__attribute__((address_space(3))) void*)(tl + kWave * k), 16, 0,
+                                       QR_ENC_NT_LOAD ? 2 : 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the DMA writes have landed
+#else
     u32x4 v[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = __builtin_nontemporal_load(src + lane + kWave * k);
+    for (int k = 0; k < 4; ++k) v[k] = ld<QR_ENC_NT_LOAD>(src + lane + kWave * k);
 #pragma unroll
     for (int k = 0; k < 4; ++k) tl[swz(lane + kWave * k)] = v[k];
+#endif
     wave_lds_sync();
     float z[kBlockValues];
 #pragma unroll
@@ -55,10 +101,12 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restr
       }
     }
     wave_lds_sync();  // the next tile overwrites this LDS tile
+    uint32_t t[kBlockValues];
+    float d;
+    const uint32_t scale = quantize_block<BITS>(z, t, d);
     Block<BITS> blk;
-    float k[kBlockValues];
-    const uint32_t scale = encode_block<BITS>(z, blk, k);
-    store_block<BITS>(packed + (size_t)tile * Format<BITS>::kTileBytes, lane, blk, scale);
+    pack_block<BITS>(t, blk);
+    store_block<BITS, QR_ENC_NT_STORE>(packed + (size_t)tile * Format<BITS>::kTileBytes, lane, blk, scale);
   }
 }
 
@@ -66,11 +114,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restr
 // decode
 // ---------------------------------------------------------------------------
 
-// Writes one lane's 32 output values (block order) and stores the wave's
-// tile in row order.
+// One lane's 32 output values (block order) into the wave's LDS tile.
 template <int DT>
-__device__ __forceinline__ void store_tile_values(u32x4* tl, int lane, const float (&y)[kBlockValues],
-                                                  uint8_t* __restrict__ dst) {
+__device__ __forceinline__ void write_lane_values(u32x4* tl, int lane, const float (&y)[kBlockValues]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     u32x4 c;
@@ -80,10 +126,15 @@ __device__ __forceinline__ void store_tile_values(u32x4* tl, int lane, const flo
     c.w = pack2<DT>(y[8 * j + 6], y[8 * j + 7]);
     tl[swz(4 * lane + j)] = c;
   }
+}
+
+// The wave's LDS tile to global memory in row order (coalesced 16-byte stores).
+template <bool NT>
+__device__ __forceinline__ void flush_tile(u32x4* tl, int lane, uint8_t* __restrict__ dst) {
   wave_lds_sync();
   u32x4* out = reinterpret_cast<u32x4*>(dst);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(tl[swz(lane + kWave * k)], out + lane + kWave * k);
+  for (int k = 0; k < 4; ++k) st<NT>(tl[swz(lane + kWave * k)], out + lane + kWave * k);
   wave_lds_sync();
 }
 
@@ -92,18 +143,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint8_t* __restr
                                                           uint8_t* __restrict__ y, int ntiles) {
   __shared__ u32x4 lds[kWavesPerGroup][kChunks];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
   for (int tile = blockIdx.x * kWavesPerGroup + wave; tile < ntiles; tile += gridDim.x * kWavesPerGroup) {
     Block<BITS> blk;
     uint32_t scale;
-    load_block<BITS>(packed + (size_t)tile * Format<BITS>::kTileBytes, lane, blk, scale);
+    load_block<BITS, QR_DEC_NT_LOAD>(packed + (size_t)tile * Format<BITS>::kTileBytes, lane, blk, scale);
     float kk[kBlockValues];
     decode_block<BITS>(blk, kk);
     const float dd = scale_f32(scale) * (1.0f / (1 << Format<BITS>::kShift));
     float v[kBlockValues];
 #pragma unroll
     for (int i = 0; i < kBlockValues; ++i) v[i] = kk[i] * dd;
-    store_tile_values<DT>(lds[wave], lane, v, y + (size_t)tile * (kTileValues * 2));
+    write_lane_values<DT>(lds[wave], lane, v);
+    flush_tile<QR_DEC_NT_STORE>(lds[wave], lane, y + (size_t)tile * (kTileValues * 2));
   }
 }
 
@@ -119,52 +171,62 @@ struct ReduceArgs {
   int ntiles;
 };
 
-template <int BITS, int DT, int RMAX, bool WITH_Y>
+template <int BITS, int DT, int R, bool WITH_Y>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
   __shared__ u32x4 lds[WITH_Y ? kWavesPerGroup : 1][WITH_Y ? kChunks : 1];
   constexpr int TB = Format<BITS>::kTileBytes;
   constexpr float kInvShift = 1.0f / (1 << Format<BITS>::kShift);
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
   for (int tile = blockIdx.x * kWavesPerGroup + wave; tile < a.ntiles; tile += gridDim.x * kWavesPerGroup) {
     const size_t toff = (size_t)tile * TB;
-    Block<BITS> blk[RMAX];
-    uint32_t sc[RMAX];
+    Block<BITS> blk[R];
+    uint32_t sc[R];
 #pragma unroll
-    for (int r = 0; r < RMAX; ++r)
-      if (r < a.R) load_block<BITS>(a.ranks[r] + toff, lane, blk[r], sc[r]);
-    // exact decode of every rank, fp32 sum in rank order
+    for (int r = 0; r < R; ++r) load_block<BITS, QR_RED_NT_LOAD>(a.ranks[r] + toff, lane, blk[r], sc[r]);
+#if QR_RED_LOADS_FIRST
+    __builtin_amdgcn_sched_barrier(0);  // every rank's loads in flight before decoding starts
+#endif
+    // exact decode of every rank, fp32 sum in rank order: s = y_0, s = s + y_r
     float s[kBlockValues];
 #pragma unroll
-    for (int r = 0; r < RMAX; ++r) {
-      if (r < a.R) {
-        float kk[kBlockValues];
-        decode_block<BITS>(blk[r], kk);
-        const float dd = scale_f32(sc[r]) * kInvShift;
-        if (r == 0) {
+    for (int r = 0; r < R; ++r) {
+      float kk[kBlockValues];
+      decode_block<BITS>(blk[r], kk);
+      const float dd = scale_f32(sc[r]) * kInvShift;
+      if (r == 0) {
 #pragma unroll
-          for (int i = 0; i < kBlockValues; ++i) s[i] = kk[i] * dd;
-        } else {
+        for (int i = 0; i < kBlockValues; ++i) s[i] = kk[i] * dd;
+      } else {
 #pragma unroll
-          for (int i = 0; i < kBlockValues; ++i) s[i] = __builtin_fmaf(kk[i], dd, s[i]);
-        }
+        for (int i = 0; i < kBlockValues; ++i) s[i] = __builtin_fmaf(kk[i], dd, s[i]);
       }
     }
-    // round the sum to the I/O dtype, re-encode
-    float z[kBlockValues];
+    // re-encode dtype_RNE(s): rounding is monotonic and symmetric, so the
+    // block maximum of the rounded values is the rounded maximum of |s|
+    float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kBlockValues; ++i) z[i] = round_to_dtype<DT>(s[i]);
-    Block<BITS> ob;
-    float k[kBlockValues];
-    const uint32_t scale = encode_block<BITS>(z, ob, k);
-    store_block<BITS>(a.out + toff, lane, ob, scale);
-    if constexpr (WITH_Y) {
-      const float d = scale_f32(scale);
+    for (int i = 0; i < kBlockValues; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(s[i]));
+    float d, e;
+    const uint32_t scale = block_scale<BITS>(round_to_dtype<DT>(m), d, e);
+    uint32_t t[kBlockValues];
+#pragma unroll
+    for (int i = 0; i < kBlockValues; i += 2) {
+      float v0, v1;
+      round_scale2<DT>(s[i], s[i + 1], e, v0, v1);
+      t[i] = quantize<BITS>(v0);
+      t[i + 1] = quantize<BITS>(v1);
+    }
+    if constexpr (WITH_Y) {  // decode of the re-encoded sum, straight from the codes
       float v[kBlockValues];
 #pragma unroll
-      for (int i = 0; i < kBlockValues; ++i) v[i] = k[i] * d;
-      store_tile_values<DT>(lds[wave], lane, v, a.y + (size_t)tile * (kTileValues * 2));
+      for (int i = 0; i < kBlockValues; ++i) v[i] = code_value<BITS>(t[i]) * d;
+      write_lane_values<DT>(lds[wave], lane, v);
     }
+    Block<BITS> ob;
+    pack_block<BITS>(t, ob);
+    store_block<BITS, QR_RED_NT_STORE>(a.out + toff, lane, ob, scale);
+    if constexpr (WITH_Y) flush_tile<QR_RED_NT_STORE>(lds[wave], lane, a.y + (size_t)tile * (kTileValues * 2));
   }
 }
 
@@ -203,21 +265,26 @@ qr_status launch_decode(int dt, const void* p, void* y, size_t ntiles, hipStream
   return hipGetLastError() == hipSuccess ? QR_OK : QR_ERR_HIP;
 }
 
-template <int BITS, int DT, int RMAX>
+template <int BITS, int DT, int R>
 void launch_reduce_r(const ReduceArgs& a, dim3 grid, hipStream_t st) {
   if (a.y)
-    hipLaunchKernelGGL((reduce_kernel<BITS, DT, RMAX, true>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((reduce_kernel<BITS, DT, R, true>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((reduce_kernel<BITS, DT, RMAX, false>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((reduce_kernel<BITS, DT, R, false>), grid, dim3(kThreads), 0, st, a);
 }
 
 template <int BITS, int DT>
 void launch_reduce_dt(const ReduceArgs& a, dim3 grid, hipStream_t st) {
-  if (a.R <= 1) launch_reduce_r<BITS, DT, 1>(a, grid, st);
-  else if (a.R <= 2) launch_reduce_r<BITS, DT, 2>(a, grid, st);
-  else if (a.R <= 4) launch_reduce_r<BITS, DT, 4>(a, grid, st);
-  else if (a.R <= 8) launch_reduce_r<BITS, DT, 8>(a, grid, st);
-  else launch_reduce_r<BITS, DT, 16>(a, grid, st);
+  switch (a.R) {
+#define QR_RANK_CASE(r) \
+  case r: launch_reduce_r<BITS, DT, r>(a, grid, st); break;
+    QR_RANK_CASE(1) QR_RANK_CASE(2) QR_RANK_CASE(3) QR_RANK_CASE(4)
+    QR_RANK_CASE(5) QR_RANK_CASE(6) QR_RANK_CASE(7) QR_RANK_CASE(8)
+    QR_RANK_CASE(9) QR_RANK_CASE(10) QR_RANK_CASE(11) QR_RANK_CASE(12)
+    QR_RANK_CASE(13) QR_RANK_CASE(14) QR_RANK_CASE(15) QR_RANK_CASE(16)
+#undef QR_RANK_CASE
+    default: break;  // R was validated to be in [1, QR_MAX_RANKS]
+  }
 }
 
 template <int BITS>

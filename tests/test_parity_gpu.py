@@ -270,3 +270,18 @@ def test_workload_full_size_sampled(qa, oracle, name):
     out_host = out.cpu().numpy() if out is not None else None
     del sel_b
     check_tiles(oracle, w, xs_t, packed_full, out_host, y_host, tiles)
+
+
+def test_block_scale_every_fp16_scale():
+    """The library's block-scale device function over every positive finite
+    fp16 scale d (block maximum Q*d): scale bits d and encode multiplier equal
+    to the correctly rounded IEEE quotient 1.0f / d, for each format."""
+    import ctypes
+    import os
+    lib = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gpu_helpers", "libscale_check.so")
+    L = ctypes.CDLL(lib)
+    L.qr_test_scale_check.argtypes = [ctypes.c_void_p]
+    counters = torch.zeros(6, dtype=torch.int32, device="cuda")
+    log("scale check over all fp16 scales")
+    assert L.qr_test_scale_check(counters.data_ptr()) == 0
+    assert counters.cpu().tolist() == [0] * 6
