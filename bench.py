@@ -257,6 +257,18 @@ def main():
         copy_ref = {"bytes": 4 * w.n, "us_per_launch": round(us, 3), "gbs": round(4 * w.n / us / 1e3, 1)}
         del dst
 
+    # quality: RMSE of the decoded result against the unquantized fp32 sum of
+    # the inputs (rank order), absolute and relative to the RMS of that sum
+    ref = xs[0].float()
+    for r in range(1, w.ranks):
+        ref += xs[r].float()
+    if not w.reduce:
+        ref = xs[0].float()
+    err = (y.float() - ref).pow(2).mean().sqrt().item()
+    rms = ref.pow(2).mean().sqrt().item()
+    rmse = {"abs": err, "rel": err / rms if rms else None}
+    del ref
+
     ab = algorithmic_bytes(w)
     launches = {"encode": w.ranks, "reduce": 1 if w.reduce else 0, "decode": 0 if w.reduce else 1}
     step_bytes = sum(ab[k] * launches[k] for k in launches)
@@ -293,6 +305,7 @@ def main():
         "pipeline_hbm_gbs": round(pipe_gbs, 1),
         "roofline": roofline,
         "kernels": kernels,
+        "rmse_vs_fp32_sum": rmse,
     }
     if copy_ref:
         result["copy_ref"] = copy_ref

@@ -27,6 +27,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileValues = 2048;
 constexpr int kBlockValues = 32;
@@ -146,11 +147,6 @@ __device__ __forceinline__ float sbyte(uint32_t x, int i) { return (float)(int8_
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ int swz(int c) { return c ^ (((c >> 2) & 5) | (((c >> 2) ^ (c >> 4)) & 2)); }
-// The chunk whose swizzled slot is s.
-__device__ __forceinline__ int unswz(int s) {
-  const int c2 = ((s >> 2) ^ (s >> 4)) & 1;
-  return s ^ (c2 | ((((s >> 3) ^ (s >> 5)) & 1) << 1) | (((s >> 4) & 1) << 2));
-}
 
 // Makes one lane's LDS writes visible to the other lanes of its wave.
 __device__ __forceinline__ void wave_lds_sync() {
@@ -273,18 +269,50 @@ __device__ __forceinline__ void pack_block(const uint32_t (&t)[kBlockValues], Bl
   }
 }
 
-// Quantizes the 32 exact dtype values z[] of one block into t[] (see
-// quantize()); returns the fp16 scale bits and sets the decode scale d.
-template <int BITS>
-__device__ __forceinline__ uint32_t quantize_block(const float (&z)[kBlockValues], uint32_t (&t)[kBlockValues],
-                                                   float& d) {
-  float m = 0.0f;
+// Largest |x| of a block held as 16 packed fp16/bf16 words, as fp32: the
+// sign bits are cleared and the magnitudes compared as unsigned 16-bit
+// integers, which orders non-negative fp16 / bf16 values (inputs are finite).
+template <int DT>
+__device__ __forceinline__ float block_absmax(const uint32_t (&w)[kBlockValues / 2]) {
+  u16x2 m = {0, 0};
 #pragma unroll
-  for (int i = 0; i < kBlockValues; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(z[i]));
-  float e;
-  const uint32_t bits = block_scale<BITS>(m, d, e);
+  for (int j = 0; j < kBlockValues / 2; ++j)
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[j] & 0x7fff7fffu));
+  const uint32_t mb = m.x > m.y ? m.x : m.y;
+  if constexpr (DT == kFp16)
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)mb);
+  else
+    return __builtin_bit_cast(float, mb << 16);
+}
+
+// RN32(x * e) for the two values of a packed fp16/bf16 word (for fp16 a
+// mixed-precision FMA reads the halves directly; fma(x, e, +0) rounds x*e once).
+template <int DT>
+__device__ __forceinline__ void scale_pair(uint32_t w, float e, float& v0, float& v1) {
+  if constexpr (DT == kFp16) {
+    const f16x2 h = __builtin_bit_cast(f16x2, w);
+    v0 = __builtin_fmaf((float)h.x, e, 0.0f);
+    v1 = __builtin_fmaf((float)h.y, e, 0.0f);
+  } else {
+    v0 = __builtin_bit_cast(float, w << 16) * e;
+    v1 = __builtin_bit_cast(float, w & 0xffff0000u) * e;
+  }
+}
+
+// Quantizes one block given as 16 packed fp16/bf16 words (value 2j in the low
+// half of word j) into t[] (see quantize()); returns the fp16 scale bits.
+template <int BITS, int DT>
+__device__ __forceinline__ uint32_t quantize_words(const uint32_t (&w)[kBlockValues / 2],
+                                                   uint32_t (&t)[kBlockValues]) {
+  float d, e;
+  const uint32_t bits = block_scale<BITS>(block_absmax<DT>(w), d, e);
 #pragma unroll
-  for (int i = 0; i < kBlockValues; ++i) t[i] = quantize<BITS>(z[i] * e);
+  for (int j = 0; j < kBlockValues / 2; ++j) {
+    float v0, v1;
+    scale_pair<DT>(w[j], e, v0, v1);
+    t[2 * j] = quantize<BITS>(v0);
+    t[2 * j + 1] = quantize<BITS>(v1);
+  }
   return bits;
 }
 
@@ -312,23 +340,22 @@ __device__ __forceinline__ void decode_block(const Block<BITS>& blk, float (&kk)
       for (int i = 0; i < 4; ++i) kk[4 * w + i] = sbyte(a, i);
     }
   } else {
+    // Values 8u + j (u = unit 0..3) are decoded together for each j: byte u
+    // of the 1-bit plane word holds unit u's high bits, so one shift puts all
+    // four (inverted: the sign of code - 4) at bit 7 of their bytes, and two
+    // byte gathers give, per unit, the low-pair byte that holds value j.
+    const uint32_t ne = ~blk.high;
+    const uint32_t p03 = __builtin_amdgcn_perm(blk.low[1], blk.low[0], 0x06040200u);  // j = 0..3
+    const uint32_t p47 = __builtin_amdgcn_perm(blk.low[1], blk.low[0], 0x07050301u);  // j = 4..7
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t low = blk.low[h];  // byte b: low pairs of values 16h + 4b + 0..3
-      // byte b bits 0..3: high bits of the same values, inverted (sign of k)
-      uint32_t x = (blk.high >> (16 * h)) & 0xffffu;
-      x = (x | (x << 8)) & 0x00FF00FFu;
-      x = (x | (x << 4)) & 0x0F0F0F0Fu;
-      const uint32_t nx = x ^ 0x0F0F0F0Fu;
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t p = j < 4 ? p03 : p47;
+      const int i = j & 3;  // the low pair sits at bits 2i..2i+1 of each byte
+      const uint32_t l = (i < 3 ? (p << (5 - 2 * i)) : (p >> 1)) & 0x60606060u;
+      // byte u = (low pair << 5) | (!high << 7) = 32 * (code - 4) as int8
+      const uint32_t b = l | ((ne << (7 - j)) & 0x80808080u);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // byte b = (low pair << 5) | (!high << 7) = 32 * (code - 4) as int8
-        const uint32_t l = (i < 3 ? (low << (5 - 2 * i)) : (low >> 1)) & 0x60606060u;
-        const uint32_t s = (nx << (7 - i)) & 0x80808080u;
-        const uint32_t b = l | s;
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) kk[16 * h + 4 * bb + i] = sbyte(b, bb);
-      }
+      for (int u = 0; u < 4; ++u) kk[8 * u + j] = sbyte(b, u);
     }
   }
 }

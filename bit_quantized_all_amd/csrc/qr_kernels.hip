@@ -47,9 +47,14 @@ namespace qr {
 #ifndef QR_RED_NT_STORE
 #define QR_RED_NT_STORE 1
 #endif
-// 1: encode loads its fp16/bf16 tile straight into LDS (global_load_lds_dwordx4).
-#ifndef QR_ENC_LDS_DMA
-#define QR_ENC_LDS_DMA 0
+// Tiles each encode wave processes (the next one prefetched while encoding).
+#ifndef QR_ENC_TILES_PER_WAVE
+#define QR_ENC_TILES_PER_WAVE 1
+#endif
+// Encode mapping: 0 = lane per 32-value block through an LDS transpose,
+// 1 = lane per 8-value unit with a 4-lane DPP block maximum.
+#ifndef QR_ENC_QUAD
+#define QR_ENC_QUAD 0
 #endif
 // 1: issue every rank's loads before decoding; 0: let the scheduler pipeline them.
 #ifndef QR_RED_LOADS_FIRST
@@ -70,43 +75,102 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restr
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
   u32x4* tl = lds[wave];
+  const int stride = gridDim.x * kWavesPerGroup;
+  int tile = blockIdx.x * kWavesPerGroup + wave;
+  if (tile >= ntiles) return;
+  // the next tile's 4 KB is loaded into registers while this one is encoded
+  u32x4 v[4];
+  auto load_tile = [&](int t) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)t * (kTileValues * 2));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = ld<QR_ENC_NT_LOAD>(src + lane + kWave * k);
+  };
+  load_tile(tile);
+  for (; tile < ntiles; tile += stride) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) tl[swz(lane + kWave * k)] = v[k];
+    if (tile + stride < ntiles) load_tile(tile + stride);
+    wave_lds_sync();
+    uint32_t w[kBlockValues / 2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 c = tl[swz(4 * lane + j)];
+      w[4 * j] = c.x; w[4 * j + 1] = c.y; w[4 * j + 2] = c.z; w[4 * j + 3] = c.w;
+    }
+    wave_lds_sync();  // the next tile overwrites this LDS tile
+    uint32_t t[kBlockValues];
+    const uint32_t scale = quantize_words<BITS, DT>(w, t);
+    Block<BITS> blk;
+    pack_block<BITS>(t, blk);
+    store_block<BITS, QR_ENC_NT_STORE>(packed + (size_t)tile * Format<BITS>::kTileBytes, lane, blk, scale);
+  }
+}
+
+// Alternative encode mapping: lane = one 8-value unit (a coalesced 16-byte
+// load straight into registers), four lanes per block; the block maximum is
+// reduced across the 4-lane group with DPP quad permutes and every lane of
+// the group derives the same scale.  No LDS.
+__device__ __forceinline__ float quad_max(float m) {
+  // quad_perm [1,0,3,2] then [2,3,0,1]
+  m = __builtin_fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0xB1, 0xF, 0xF, false)));
+  m = __builtin_fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0x4E, 0xF, 0xF, false)));
+  return m;
+}
+
+template <int BITS, int DT>
+__global__ __launch_bounds__(kThreads) void encode_quad_kernel(const uint8_t* __restrict__ x,
+                                                               uint8_t* __restrict__ packed, int ntiles) {
+  constexpr int TB = Format<BITS>::kTileBytes;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   for (int tile = blockIdx.x * kWavesPerGroup + wave; tile < ntiles; tile += gridDim.x * kWavesPerGroup) {
     const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)tile * (kTileValues * 2));
-#if QR_ENC_LDS_DMA
-    // global -> LDS without VGPRs: instruction k writes slot 64k + lane, so lane
-    // fetches the chunk that the swizzle maps there (still one 1 KB span).
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      __builtin_amdgcn_global_load_lds(src + unswz(kWave * k + lane),
-                                       (__attribute__((address_space(3))) void*)(tl + kWave * k), 16, 0,
-                                       QR_ENC_NT_LOAD ? 2 : 0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the DMA writes have landed
-#else
+    uint8_t* dst = packed + (size_t)tile * TB;
     u32x4 v[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) v[k] = ld<QR_ENC_NT_LOAD>(src + lane + kWave * k);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) tl[swz(lane + kWave * k)] = v[k];
-#endif
-    wave_lds_sync();
-    float z[kBlockValues];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 c = tl[swz(4 * lane + j)];
-      const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    for (int k = 0; k < 4; ++k) {
+      const int u = kWave * k + lane;  // unit index in the tile
+      const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+      float z[8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        z[8 * j + 2 * q] = lo_to_f32<DT>(w[q]);
-        z[8 * j + 2 * q + 1] = hi_to_f32<DT>(w[q]);
+        z[2 * q] = lo_to_f32<DT>(w[q]);
+        z[2 * q + 1] = hi_to_f32<DT>(w[q]);
       }
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(z[i]));
+      m = quad_max(m);
+      float d, e;
+      const uint32_t scale = block_scale<BITS>(m, d, e);
+      uint32_t t[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t[i] = quantize<BITS>(z[i] * e);
+      if constexpr (BITS == 4) {
+        st<QR_ENC_NT_STORE>(pack_int4_unit(t), reinterpret_cast<uint32_t*>(dst + 4 * u));
+      } else if constexpr (BITS == 8) {
+        st<QR_ENC_NT_STORE>(u32x2{pack_int8_word(t), pack_int8_word(t + 4)}, reinterpret_cast<u32x2*>(dst + 8 * u));
+      } else {
+        // bytes c0 c2 c4 c6 and c1 c3 c5 c7 -> 2-bit plane word and 1-bit plane byte
+        const uint32_t ev = lo_pair(t[0], t[2]) | hi_pair(t[4], t[6]);
+        const uint32_t od = lo_pair(t[1], t[3]) | hi_pair(t[5], t[7]);
+        const uint32_t nib = ev | (od << 4);           // nibble j = code j (INT4 order)
+        uint32_t lo = nib & 0x33333333u;               // low pairs at bits 4j
+        lo = (lo | (lo >> 2)) & 0x0F0F0F0Fu;
+        lo = (lo | (lo >> 4)) & 0x00FF00FFu;
+        lo = (lo | (lo >> 8)) & 0x0000FFFFu;
+        uint32_t hb = (nib >> 2) & 0x11111111u;        // high bits at bits 4j
+        hb = (hb | (hb >> 3)) & 0x03030303u;
+        hb = (hb | (hb >> 6)) & 0x000F000Fu;
+        hb = (hb | (hb >> 12)) & 0x000000FFu;
+        st<QR_ENC_NT_STORE>((uint16_t)lo, reinterpret_cast<uint16_t*>(dst + 2 * u));
+        st<QR_ENC_NT_STORE>((uint8_t)hb, dst + Format<3>::kHighOffset + u);
+      }
+      if ((lane & 3) == 0)
+        st<QR_ENC_NT_STORE>((uint16_t)scale, reinterpret_cast<uint16_t*>(dst + Format<BITS>::kScaleOffset + 2 * (u >> 2)));
     }
-    wave_lds_sync();  // the next tile overwrites this LDS tile
-    uint32_t t[kBlockValues];
-    float d;
-    const uint32_t scale = quantize_block<BITS>(z, t, d);
-    Block<BITS> blk;
-    pack_block<BITS>(t, blk);
-    store_block<BITS, QR_ENC_NT_STORE>(packed + (size_t)tile * Format<BITS>::kTileBytes, lane, blk, scale);
   }
 }
 
@@ -243,13 +307,19 @@ inline dim3 grid_for(size_t ntiles) {
 
 template <int BITS>
 qr_status launch_encode(int dt, const void* x, void* p, size_t ntiles, hipStream_t st) {
-  const dim3 grid = grid_for(ntiles);
+  const dim3 grid = grid_for((ntiles + QR_ENC_TILES_PER_WAVE - 1) / QR_ENC_TILES_PER_WAVE);
+#if QR_ENC_QUAD
+#define QR_ENCODE_KERNEL encode_quad_kernel
+#else
+#define QR_ENCODE_KERNEL encode_kernel
+#endif
   if (dt == kFp16)
-    hipLaunchKernelGGL((encode_kernel<BITS, kFp16>), grid, dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((QR_ENCODE_KERNEL<BITS, kFp16>), grid, dim3(kThreads), 0, st,
                        (const uint8_t*)x, (uint8_t*)p, (int)ntiles);
   else
-    hipLaunchKernelGGL((encode_kernel<BITS, kBf16>), grid, dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((QR_ENCODE_KERNEL<BITS, kBf16>), grid, dim3(kThreads), 0, st,
                        (const uint8_t*)x, (uint8_t*)p, (int)ntiles);
+#undef QR_ENCODE_KERNEL
   return hipGetLastError() == hipSuccess ? QR_OK : QR_ERR_HIP;
 }
 

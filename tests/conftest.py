@@ -10,6 +10,12 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    # Use what is built; build only what is missing.
+    from bit_quantized_all_amd import build as hip_build
+    if not os.path.exists(hip_build.LIB):
+        hip_build.build()
+    if not os.path.exists(hip_build.TEST_HELPER_LIB):
+        hip_build.build_test_helpers()
 
 
 @pytest.fixture(scope="session")
