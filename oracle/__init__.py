@@ -62,6 +62,9 @@ class Oracle:
         L.qro_reduce.restype = ctypes.c_int
         L.qro_reduce.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(_u8p), ctypes.c_int,
                                  _u8p, _u16p, ctypes.c_size_t]
+        L.qro_reduce_mixed.restype = ctypes.c_int
+        L.qro_reduce_mixed.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(_u8p),
+                                       ctypes.c_int, _u8p, _u16p, ctypes.c_size_t]
         L.qro_block_scale.restype = None
         L.qro_block_scale.argtypes = [ctypes.c_int, ctypes.c_float, _u16p, _f32p]
         L.qro_f16_to_f32.restype = ctypes.c_float
@@ -118,6 +121,18 @@ class Oracle:
                                _ptr(y, _u16p) if with_output else None, n)
         if rc:
             raise ValueError("qro_reduce rejected its arguments")
+        return out, y
+
+    def reduce_mixed(self, fmt_in, fmt_out, dtype, ranks, n, with_output=True):
+        """Inputs packed in fmt_in, re-encoded sum in fmt_out; returns (packed_out, y_out or None)."""
+        ranks = [np.ascontiguousarray(r, dtype=np.uint8) for r in ranks]
+        arr = (_u8p * len(ranks))(*[_ptr(r, _u8p) for r in ranks])
+        out = np.zeros(self.packed_bytes(fmt_out, n), np.uint8)
+        y = np.zeros(n, np.uint16) if with_output else None
+        rc = self.L.qro_reduce_mixed(_fmt(fmt_in), _fmt(fmt_out), _dt(dtype), arr, len(ranks),
+                                     _ptr(out, _u8p), _ptr(y, _u16p) if with_output else None, n)
+        if rc:
+            raise ValueError("qro_reduce_mixed rejected its arguments")
         return out, y
 
     # -- helpers exposed for pinning -----------------------------------------

@@ -315,12 +315,17 @@ int qro_decode(int fmt, int dtype, const uint8_t *packed, uint16_t *y, size_t n)
   return 0;
 }
 
-/* Compressed-domain reduction over R rank buffers (R6, [QR-Q], [FC]). */
-int qro_reduce(int fmt, int dtype, const uint8_t *const *ranks, int R, uint8_t *packed_out,
-               uint16_t *y_out, size_t n) {
-  if (check(fmt, dtype, n) || R < 1) return -1;
-  int bits = fmt_bits(fmt);
-  size_t tb = tile_bytes(bits);
+/* Compressed-domain reduction over R rank buffers (R6, [QR-Q], [FC]), with
+   the inputs in format fmt_in and the re-encoded sum in fmt_out.  Mixed
+   formats per phase follow the Flash Communication review's "INT6"
+   configuration (fields minor_comments, section 3.2.3, and
+   forward_implications): 4-bit codes for the reduce-scatter inputs, 8-bit
+   codes for the all-gather payload. */
+int qro_reduce_mixed(int fmt_in, int fmt_out, int dtype, const uint8_t *const *ranks, int R,
+                     uint8_t *packed_out, uint16_t *y_out, size_t n) {
+  if (check(fmt_in, dtype, n) || check(fmt_out, dtype, n) || R < 1) return -1;
+  int bits = fmt_bits(fmt_in), obits = fmt_bits(fmt_out);
+  size_t tb = tile_bytes(bits), otb = tile_bytes(obits);
   float z[QRO_TILE];
   for (size_t t = 0; t < n / QRO_TILE; ++t) {
     for (int i = 0; i < QRO_TILE; ++i) {
@@ -328,13 +333,19 @@ int qro_reduce(int fmt, int dtype, const uint8_t *const *ranks, int R, uint8_t *
       for (int r = 1; r < R; ++r) s = s + decode_value(bits, ranks[r] + t * tb, i);
       z[i] = dtype_to_f32(dtype, f32_to_dtype(dtype, s));
     }
-    uint8_t *out = packed_out + t * tb;
-    encode_tile(bits, z, out);
+    uint8_t *out = packed_out + t * otb;
+    encode_tile(obits, z, out);
     if (y_out)
       for (int i = 0; i < QRO_TILE; ++i)
-        y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value(bits, out, i));
+        y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value(obits, out, i));
   }
   return 0;
+}
+
+/* The same-format reduction. */
+int qro_reduce(int fmt, int dtype, const uint8_t *const *ranks, int R, uint8_t *packed_out,
+               uint16_t *y_out, size_t n) {
+  return qro_reduce_mixed(fmt, fmt, dtype, ranks, R, packed_out, y_out, n);
 }
 
 /* Array forms of the conversions above, for the converter pins. */

@@ -642,6 +642,68 @@ def pin_reduce_exact_terms(o):
 
 
 # ---------------------------------------------------------------------------
+# mixed formats per phase (inputs in one format, re-encoded sum in another)
+# ---------------------------------------------------------------------------
+
+MIXED = [(4, 8), (3, 4), (3, 8), (8, 4), (4, 3)]
+
+
+def pin_reduce_mixed_r1_composition(o, seed=9):
+    """R = 1 with input format a and output format b: the packed result is the
+    encoding in b of dtype_RNE(exact decode of a) (rounding by numpy / torch),
+    and the output is dtype_RNE of its exact decode in b."""
+    rng = np.random.default_rng(seed)
+    for a, b in MIXED:
+        Qb = qmax(b)
+        for dtype in DTYPES:
+            n = 2 * TILE
+            xb = _rng_blocks(rng, dtype, n // BLOCK)
+            p = o.encode(a, dtype, xb)
+            codes, sb = unpack(a, p)
+            exact = ((codes - qmax(a)).reshape(-1, 64, BLOCK) * f16_value(sb)[:, :, None]).ravel()
+            zb = f16_bits(exact) if dtype == "fp16" else bf16_bits(exact)
+            out, y = o.reduce_mixed(a, b, dtype, [p], n)
+            assert out.size == P_bytes(b, n)
+            assert np.array_equal(out, o.encode(b, dtype, zb)), (a, b, dtype)
+            c2, s2 = unpack(b, out)
+            ex2 = ((c2 - Qb).reshape(-1, 64, BLOCK) * f16_value(s2)[:, :, None]).ravel()
+            assert np.array_equal(y, f16_bits(ex2) if dtype == "fp16" else bf16_bits(ex2)), (a, b, dtype)
+
+
+def P_bytes(bits, n):
+    return n // TILE * tile_bytes(bits)
+
+
+def pin_reduce_mixed_exact(o, seed=10):
+    """INT4 inputs sharing a power-of-two scale s over R = 8 ranks, integer sums
+    in [-64, 63] with one element at -64: the INT8 re-encode has scale s/2 and
+    codes 2*sum + 128, and the output equals the exact sum.  Likewise INT3
+    inputs over R = 2 (sums in [-8, 6], one at -8) re-encoded in INT4 with
+    scale s and codes sum + 8."""
+    rng = np.random.default_rng(seed)
+    for a, b, R, lo, hi in ((4, 8, 8, -64, 63), (3, 4, 2, -8, 6)):
+        Qa = qmax(a)
+        for dtype in DTYPES:
+            nb = 128
+            k = rng.integers(-Qa, Qa, size=(R, nb, BLOCK))
+            k[:, :, 0] = -Qa                    # every rank's anchor; element 0 sums to -R*Qa
+            tot = k.sum(axis=0)
+            assert tot[:, 0].min() == lo
+            k = np.where((tot > hi)[None], 0, k)
+            k[:, :, 0] = -Qa
+            tot = k.sum(axis=0)
+            assert np.all((tot >= lo) & (tot <= hi))
+            s = 2.0 ** rng.integers(-8, 3, size=nb)
+            ranks = [o.encode(a, dtype, dtype_bits(dtype, (k[r] * s[:, None]).ravel())) for r in range(R)]
+            out, y = o.reduce_mixed(a, b, dtype, ranks, nb * BLOCK)
+            codes, sb = unpack(b, out)
+            scale = s * (-lo) / qmax(b)          # 2^-1 * s for (4, 8), s for (3, 4)
+            assert np.array_equal(sb.ravel(), f16_bits(scale)), (a, b, dtype)
+            assert np.array_equal(codes.reshape(nb, BLOCK), (tot / (scale / s)[:, None]).astype(np.int64) + qmax(b))
+            assert np.array_equal(y, dtype_bits(dtype, (tot * s[:, None]).ravel())), (a, b, dtype)
+
+
+# ---------------------------------------------------------------------------
 # P8: error bound of encode -> reduce -> decode against the exact sum
 # ---------------------------------------------------------------------------
 
@@ -700,5 +762,7 @@ ALL_PINS = [
     pin_reduce_exact_common_scale,
     pin_reduce_rank_order,
     pin_reduce_exact_terms,
+    pin_reduce_mixed_r1_composition,
+    pin_reduce_mixed_exact,
     pin_error_bound,
 ]

@@ -83,8 +83,12 @@ MUTANTS = [
     ("fp16 subnormal decode scale", [("mag = ldexpf((float)frac, -24);", "mag = ldexpf((float)frac, -25);")]),
     ("block of 16 values", [("#define QRO_BLOCK 32 ", "#define QRO_BLOCK 16 ")]),
     ("output decoded before re-encode", [
-        ("y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value(bits, out, i));",
+        ("y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value(obits, out, i));",
          "y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, z[i]);")]),
+    ("mixed: re-encode in the input format", [("encode_tile(obits, z, out);", "encode_tile(bits, z, out);")]),
+    ("mixed: final decode in the input format", [
+        ("y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value(obits, out, i));",
+         "y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value(bits, out, i));")]),
 ]
 
 
