@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GB/s of FP16 input through encode+compressed-reduce+decode; % HBM peak"
 PEAK_HBM_GBS = 8000.0
 TILE_BYTES = {"int3": 896, "int4": 1152, "int8": 2176}
-KERNEL_SOURCES = ["bit_quantized_all_amd/csrc/qr_kernels.hip", "bit_quantized_all_amd/csrc/qr_codec.hpp"]
+KERNEL_SOURCES = ["bit_quantized_all_amd/csrc/qr_kernels.hpp", "bit_quantized_all_amd/csrc/qr_codec.hpp"]
 
 
 def kernel_source_hash():
@@ -42,9 +42,10 @@ def kernel_source_hash():
 def algorithmic_bytes(w):
     """Bytes each kernel must move per launch (compressed buffers in HBM are the wire)."""
     c = TILE_BYTES[w.fmt] / 2048
+    co = TILE_BYTES[w.out_fmt] / 2048
     n = w.n
     out = {"encode": n * (2 + c), "decode": n * (c + 2)}
-    out["reduce"] = n * (w.ranks * c + c + 2)
+    out["reduce"] = n * (w.ranks * c + co + 2)
     return out
 
 
@@ -121,7 +122,8 @@ def cpu_baseline(w, xs, out, y, seconds):
 
     o = oracle.default()
     bits = {"int3": 3, "int4": 4, "int8": 8}[w.fmt]
-    tb = TILE_BYTES[w.fmt]
+    obits = {"int3": 3, "int4": 4, "int8": 8}[w.out_fmt]
+    tb = TILE_BYTES[w.out_fmt]
     ntiles = w.n // 2048
     chunk = 16
     done = 0
@@ -134,7 +136,7 @@ def cpu_baseline(w, xs, out, y, seconds):
         t0 = time.perf_counter()
         packed = [o.encode(bits, w.io_dtype, h) for h in host]
         if w.reduce:
-            po, yo = o.reduce(bits, w.io_dtype, packed, chunk * 2048)
+            po, yo = o.reduce_mixed(bits, obits, w.io_dtype, packed, chunk * 2048)
         else:
             po, yo = None, o.decode(bits, w.io_dtype, packed[0], chunk * 2048)
         busy += time.perf_counter() - t0
@@ -190,7 +192,7 @@ def main():
     xs = W.inputs(w, seed=args.seed, device=dev)
     pb = qa.qr_packed_bytes(w.fmt, w.n)
     packed = [torch.empty(pb, dtype=torch.uint8, device=dev) for _ in range(w.ranks)]
-    out = torch.empty(pb, dtype=torch.uint8, device=dev) if w.reduce else None
+    out = torch.empty(qa.qr_packed_bytes(w.out_fmt, w.n), dtype=torch.uint8, device=dev) if w.reduce else None
     y = torch.empty(w.n, dtype=w.dtype, device=dev)
     torch.cuda.synchronize()
 
@@ -199,7 +201,8 @@ def main():
 
     def finish():
         if w.reduce:
-            qa.qr_reduce_compressed(w.fmt, w.dtype, packed, w.n, packed_out=out, y_out=y, stream=stream)
+            qa.qr_reduce_compressed_mixed(w.fmt, w.out_fmt, w.dtype, packed, w.n, packed_out=out, y_out=y,
+                                          stream=stream)
         else:
             qa.qr_decode(w.fmt, packed[0], w.n, w.dtype, y=y, stream=stream)
 
@@ -299,7 +302,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": name, "format": w.fmt, "io_dtype": w.io_dtype, "ranks": w.ranks,
+        "config": {"workload": name, "format": w.fmt, "format_out": w.out_fmt, "io_dtype": w.io_dtype,
+                   "ranks": w.ranks,
                    "values_per_rank": w.n, "shape": list(w.shape), "seed": args.seed},
         "pct_hbm_peak": round(100 * pipe_gbs / PEAK_HBM_GBS, 2),
         "pipeline_hbm_gbs": round(pipe_gbs, 1),

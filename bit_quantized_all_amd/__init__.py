@@ -4,4 +4,4 @@ The kernels live in ``csrc/`` and are built into ``libqr.so``; ``qr`` is the
 ctypes binding of the C ABI declared in ``include/qr.h``.
 """
 from .qr import (FORMATS, MAX_RANKS, QRError, TILE_VALUES, lib, qr_decode, qr_encode,  # noqa: F401
-                 qr_packed_bytes, qr_reduce_compressed, qr_status_string)
+                 qr_packed_bytes, qr_reduce_compressed, qr_reduce_compressed_mixed, qr_status_string)

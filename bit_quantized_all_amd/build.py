@@ -11,12 +11,15 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "qr_kernels.hip")
+_CSRC = os.path.join(HERE, "csrc")
+# (source, extra flags): the mixed-format reduce is built once per input format
+SOURCES = [(os.path.join(_CSRC, "qr_api.hip"), [])] + [
+    (os.path.join(_CSRC, "qr_reduce_mixed.hip"), [f"-DQR_MIXED_IN={b}"]) for b in (3, 4, 8)]
 LIB = os.path.join(HERE, "libqr.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
@@ -24,16 +27,34 @@ FLAGS = [
 ]
 
 
-def build(out=LIB, extra=(), quiet=True, src=SRC):
-    """Compile the kernels and the C ABI into ``out``; returns ``out``."""
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, src]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"HIP build failed: {' '.join(cmd)}\n{res.stderr}")
-    if not quiet and res.stderr:
-        sys.stderr.write(res.stderr)
-    os.replace(tmp, out)
+def _run(cmd):
+    return subprocess.run(cmd, capture_output=True, text=True)
+
+
+def build(out=LIB, extra=(), quiet=True, sources=None):
+    """Compile the translation units in parallel and link them into ``out``."""
+    import concurrent.futures
+    import tempfile
+
+    sources = SOURCES if sources is None else sources
+    with tempfile.TemporaryDirectory() as tmpdir:
+        sources = [s if isinstance(s, tuple) else (s, []) for s in sources]
+        objs = [os.path.join(tmpdir, f"{i}_{os.path.basename(src)}.o") for i, (src, _) in enumerate(sources)]
+        cmds = [[HIPCC, *FLAGS, *extra, *defs, "-c", "-o", obj, src]
+                for (src, defs), obj in zip(sources, objs)]
+        with concurrent.futures.ThreadPoolExecutor(len(cmds)) as ex:
+            results = list(ex.map(_run, cmds))
+        for cmd, res in zip(cmds, results):
+            if res.returncode != 0:
+                raise RuntimeError(f"HIP build failed: {' '.join(cmd)}\n{res.stderr}")
+            if not quiet and res.stderr:
+                sys.stderr.write(res.stderr)
+        tmp = out + ".tmp"
+        link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+        res = _run(link)
+        if res.returncode != 0:
+            raise RuntimeError(f"HIP link failed: {' '.join(link)}\n{res.stderr}")
+        os.replace(tmp, out)
     return out
 
 
@@ -43,7 +64,7 @@ TEST_HELPER_LIB = os.path.join(ROOT, "tests", "gpu_helpers", "libscale_check.so"
 
 def build_test_helpers(quiet=True):
     """Test-only HIP helper that exercises the codec's device functions directly."""
-    return build(out=TEST_HELPER_LIB, src=TEST_HELPER_SRC, quiet=quiet)
+    return build(out=TEST_HELPER_LIB, sources=[TEST_HELPER_SRC], quiet=quiet)
 
 
 if __name__ == "__main__":

@@ -1,19 +1,23 @@
-// qr_kernels.hip -- gfx950 kernels and the C ABI declared in include/qr.h.
+// qr_kernels.hpp -- gfx950 kernels and their launch helpers (the C ABI that
+// calls them is in qr_api.hip; mixed-format reduce instantiations are in
+// qr_reduce_mixed.hip).
 //
 // Three kernels, each with one 64-lane wave per 2048-value tile and one lane
 // per 32-value block (the codec itself is in qr_codec.hpp):
 //   encode  fp16/bf16 tile -> LDS (row order) -> lane block -> packed tile
 //   decode  packed block -> lane -> LDS (block order) -> fp16/bf16 tile
 //   reduce  R packed blocks -> exact fp32 decode + rank-order sum -> round to
-//           dtype -> re-encode (packed_out) -> decode (y_out, through LDS)
+//           dtype -> re-encode (packed_out) -> decode (y_out, through LDS);
+//           the inputs and the re-encoded sum may use different formats
 // The reduce is the in-segment reduction + re-quantization of the two-shot
 // all-reduce ("QuickReduce INT3 quantization and benchmarking on MI355",
 // "Quantization and Dequantization Paths"; "Flash Communication" review,
 // key_machinery): two quantization round trips, decode-sum-encode fused so
 // that the fp32 sum never leaves registers.
+#pragma once
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <string.h>
 
 #include "qr.h"
 #include "qr_codec.hpp"
@@ -235,19 +239,20 @@ struct ReduceArgs {
   int ntiles;
 };
 
-template <int BITS, int DT, int R, bool WITH_Y>
+template <int BI, int BO, int DT, int R, bool WITH_Y>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
   __shared__ u32x4 lds[WITH_Y ? kWavesPerGroup : 1][WITH_Y ? kChunks : 1];
-  constexpr int TB = Format<BITS>::kTileBytes;
-  constexpr float kInvShift = 1.0f / (1 << Format<BITS>::kShift);
+  constexpr int TB = Format<BI>::kTileBytes;    // input tiles
+  constexpr int TBO = Format<BO>::kTileBytes;   // re-encoded tiles
+  constexpr float kInvShift = 1.0f / (1 << Format<BI>::kShift);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
   for (int tile = blockIdx.x * kWavesPerGroup + wave; tile < a.ntiles; tile += gridDim.x * kWavesPerGroup) {
     const size_t toff = (size_t)tile * TB;
-    Block<BITS> blk[R];
+    Block<BI> blk[R];
     uint32_t sc[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) load_block<BITS, QR_RED_NT_LOAD>(a.ranks[r] + toff, lane, blk[r], sc[r]);
+    for (int r = 0; r < R; ++r) load_block<BI, QR_RED_NT_LOAD>(a.ranks[r] + toff, lane, blk[r], sc[r]);
 #if QR_RED_LOADS_FIRST
     __builtin_amdgcn_sched_barrier(0);  // every rank's loads in flight before decoding starts
 #endif
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float kk[kBlockValues];
-      decode_block<BITS>(blk[r], kk);
+      decode_block<BI>(blk[r], kk);
       const float dd = scale_f32(sc[r]) * kInvShift;
       if (r == 0) {
 #pragma unroll
@@ -272,24 +277,24 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
 #pragma unroll
     for (int i = 0; i < kBlockValues; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(s[i]));
     float d, e;
-    const uint32_t scale = block_scale<BITS>(round_to_dtype<DT>(m), d, e);
+    const uint32_t scale = block_scale<BO>(round_to_dtype<DT>(m), d, e);
     uint32_t t[kBlockValues];
 #pragma unroll
     for (int i = 0; i < kBlockValues; i += 2) {
       float v0, v1;
       round_scale2<DT>(s[i], s[i + 1], e, v0, v1);
-      t[i] = quantize<BITS>(v0);
-      t[i + 1] = quantize<BITS>(v1);
+      t[i] = quantize<BO>(v0);
+      t[i + 1] = quantize<BO>(v1);
     }
     if constexpr (WITH_Y) {  // decode of the re-encoded sum, straight from the codes
       float v[kBlockValues];
 #pragma unroll
-      for (int i = 0; i < kBlockValues; ++i) v[i] = code_value<BITS>(t[i]) * d;
+      for (int i = 0; i < kBlockValues; ++i) v[i] = code_value<BO>(t[i]) * d;
       write_lane_values<DT>(lds[wave], lane, v);
     }
-    Block<BITS> ob;
-    pack_block<BITS>(t, ob);
-    store_block<BITS, QR_RED_NT_STORE>(a.out + toff, lane, ob, scale);
+    Block<BO> ob;
+    pack_block<BO>(t, ob);
+    store_block<BO, QR_RED_NT_STORE>(a.out + (size_t)tile * TBO, lane, ob, scale);
     if constexpr (WITH_Y) flush_tile<QR_RED_NT_STORE>(lds[wave], lane, a.y + (size_t)tile * (kTileValues * 2));
   }
 }
@@ -335,19 +340,19 @@ qr_status launch_decode(int dt, const void* p, void* y, size_t ntiles, hipStream
   return hipGetLastError() == hipSuccess ? QR_OK : QR_ERR_HIP;
 }
 
-template <int BITS, int DT, int R>
+template <int BI, int BO, int DT, int R>
 void launch_reduce_r(const ReduceArgs& a, dim3 grid, hipStream_t st) {
   if (a.y)
-    hipLaunchKernelGGL((reduce_kernel<BITS, DT, R, true>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((reduce_kernel<BI, BO, DT, R, true>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((reduce_kernel<BITS, DT, R, false>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((reduce_kernel<BI, BO, DT, R, false>), grid, dim3(kThreads), 0, st, a);
 }
 
-template <int BITS, int DT>
+template <int BI, int BO, int DT>
 void launch_reduce_dt(const ReduceArgs& a, dim3 grid, hipStream_t st) {
   switch (a.R) {
 #define QR_RANK_CASE(r) \
-  case r: launch_reduce_r<BITS, DT, r>(a, grid, st); break;
+  case r: launch_reduce_r<BI, BO, DT, r>(a, grid, st); break;
     QR_RANK_CASE(1) QR_RANK_CASE(2) QR_RANK_CASE(3) QR_RANK_CASE(4)
     QR_RANK_CASE(5) QR_RANK_CASE(6) QR_RANK_CASE(7) QR_RANK_CASE(8)
     QR_RANK_CASE(9) QR_RANK_CASE(10) QR_RANK_CASE(11) QR_RANK_CASE(12)
@@ -357,127 +362,18 @@ void launch_reduce_dt(const ReduceArgs& a, dim3 grid, hipStream_t st) {
   }
 }
 
-template <int BITS>
+template <int BI, int BO>
 qr_status launch_reduce(int dt, const ReduceArgs& a, hipStream_t st) {
   const dim3 grid = grid_for((size_t)a.ntiles);
-  if (dt == kFp16) launch_reduce_dt<BITS, kFp16>(a, grid, st);
-  else launch_reduce_dt<BITS, kBf16>(a, grid, st);
+  if (dt == kFp16) launch_reduce_dt<BI, BO, kFp16>(a, grid, st);
+  else launch_reduce_dt<BI, BO, kBf16>(a, grid, st);
   return hipGetLastError() == hipSuccess ? QR_OK : QR_ERR_HIP;
 }
 
-// ---------------------------------------------------------------------------
-// host-side argument checks (no HIP call)
-// ---------------------------------------------------------------------------
-
-inline int tile_bytes(int fmt) {
-  switch (fmt) {
-    case QR_INT3: return Format<3>::kTileBytes;
-    case QR_INT4: return Format<4>::kTileBytes;
-    case QR_INT8: return Format<8>::kTileBytes;
-    default: return 0;
-  }
-}
-
-inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
-inline bool overlap(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-  return a0 < b0 + nb && b0 < a0 + na;
-}
-
-// Too many tiles for the kernels' int tile index.
-inline bool too_large(size_t n) { return n / kTileValues > (size_t)0x7fffffff; }
+// Reduce with input format != output format (instantiated in qr_reduce_mixed.hip,
+// one object per input format).
+qr_status launch_reduce_mixed_from3(int fmt_out, int dt, const ReduceArgs& a, hipStream_t st);
+qr_status launch_reduce_mixed_from4(int fmt_out, int dt, const ReduceArgs& a, hipStream_t st);
+qr_status launch_reduce_mixed_from8(int fmt_out, int dt, const ReduceArgs& a, hipStream_t st);
 
 }  // namespace qr
-
-using namespace qr;
-
-extern "C" {
-
-size_t qr_packed_bytes(qr_format fmt, size_t n) {
-  const int tb = tile_bytes(fmt);
-  if (!tb || n % kTileValues) return 0;
-  return n / kTileValues * (size_t)tb;
-}
-
-qr_status qr_encode(qr_format fmt, qr_dtype dtype, const void* x, void* packed, size_t n, void* stream) {
-  if (!tile_bytes(fmt) || (dtype != QR_FP16 && dtype != QR_BF16)) return QR_ERR_UNSUPPORTED;
-  if (n % kTileValues || too_large(n)) return QR_ERR_SIZE;
-  if (n == 0) return QR_OK;
-  if (!x || !packed) return QR_ERR_ARG;
-  if (!aligned16(x) || !aligned16(packed)) return QR_ERR_ALIGN;
-  const size_t pb = qr_packed_bytes(fmt, n);
-  if (overlap(x, 2 * n, packed, pb)) return QR_ERR_ALIAS;
-  const size_t nt = n / kTileValues;
-  hipStream_t st = (hipStream_t)stream;
-  switch (fmt) {
-    case QR_INT3: return launch_encode<3>(dtype, x, packed, nt, st);
-    case QR_INT4: return launch_encode<4>(dtype, x, packed, nt, st);
-    default: return launch_encode<8>(dtype, x, packed, nt, st);
-  }
-}
-
-qr_status qr_decode(qr_format fmt, qr_dtype dtype, const void* packed, void* y, size_t n, void* stream) {
-  if (!tile_bytes(fmt) || (dtype != QR_FP16 && dtype != QR_BF16)) return QR_ERR_UNSUPPORTED;
-  if (n % kTileValues || too_large(n)) return QR_ERR_SIZE;
-  if (n == 0) return QR_OK;
-  if (!packed || !y) return QR_ERR_ARG;
-  if (!aligned16(packed) || !aligned16(y)) return QR_ERR_ALIGN;
-  const size_t pb = qr_packed_bytes(fmt, n);
-  if (overlap(y, 2 * n, packed, pb)) return QR_ERR_ALIAS;
-  const size_t nt = n / kTileValues;
-  hipStream_t st = (hipStream_t)stream;
-  switch (fmt) {
-    case QR_INT3: return launch_decode<3>(dtype, packed, y, nt, st);
-    case QR_INT4: return launch_decode<4>(dtype, packed, y, nt, st);
-    default: return launch_decode<8>(dtype, packed, y, nt, st);
-  }
-}
-
-qr_status qr_reduce_compressed(qr_format fmt, qr_dtype dtype, const void* const* packed_ranks, int R,
-                               void* packed_out, void* y_out, size_t n, void* stream) {
-  if (!tile_bytes(fmt) || (dtype != QR_FP16 && dtype != QR_BF16)) return QR_ERR_UNSUPPORTED;
-  if (R < 1 || R > QR_MAX_RANKS) return QR_ERR_ARG;
-  if (n % kTileValues || too_large(n)) return QR_ERR_SIZE;
-  if (n == 0) return QR_OK;
-  if (!packed_ranks || !packed_out) return QR_ERR_ARG;
-  for (int r = 0; r < R; ++r)
-    if (!packed_ranks[r]) return QR_ERR_ARG;
-  for (int r = 0; r < R; ++r)
-    if (!aligned16(packed_ranks[r])) return QR_ERR_ALIGN;
-  if (!aligned16(packed_out) || (y_out && !aligned16(y_out))) return QR_ERR_ALIGN;
-  const size_t pb = qr_packed_bytes(fmt, n);
-  for (int r = 0; r < R; ++r) {
-    if (overlap(packed_ranks[r], pb, packed_out, pb)) return QR_ERR_ALIAS;
-    if (y_out && overlap(packed_ranks[r], pb, y_out, 2 * n)) return QR_ERR_ALIAS;
-  }
-  if (y_out && overlap(packed_out, pb, y_out, 2 * n)) return QR_ERR_ALIAS;
-  ReduceArgs a;
-  memset(&a, 0, sizeof a);
-  for (int r = 0; r < R; ++r) a.ranks[r] = (const uint8_t*)packed_ranks[r];
-  a.out = (uint8_t*)packed_out;
-  a.y = (uint8_t*)y_out;
-  a.R = R;
-  a.ntiles = (int)(n / kTileValues);
-  hipStream_t st = (hipStream_t)stream;
-  switch (fmt) {
-    case QR_INT3: return launch_reduce<3>(dtype, a, st);
-    case QR_INT4: return launch_reduce<4>(dtype, a, st);
-    default: return launch_reduce<8>(dtype, a, st);
-  }
-}
-
-const char* qr_status_string(qr_status s) {
-  switch (s) {
-    case QR_OK: return "ok";
-    case QR_ERR_ARG: return "invalid argument (null pointer or rank count)";
-    case QR_ERR_SIZE: return "value count is not a multiple of 2048";
-    case QR_ERR_ALIGN: return "buffer pointer is not 16-byte aligned";
-    case QR_ERR_UNSUPPORTED: return "unsupported format or dtype";
-    case QR_ERR_ALIAS: return "output buffer overlaps another buffer";
-    case QR_ERR_HIP: return "HIP launch error";
-  }
-  return "unknown status";
-}
-
-}  // extern "C"

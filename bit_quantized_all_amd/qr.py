@@ -43,6 +43,8 @@ def lib():
         L.qr_decode.argtypes = [i, i, vp, vp, sz, vp]
         L.qr_reduce_compressed.restype = i
         L.qr_reduce_compressed.argtypes = [i, i, ctypes.POINTER(vp), i, vp, vp, sz, vp]
+        L.qr_reduce_compressed_mixed.restype = i
+        L.qr_reduce_compressed_mixed.argtypes = [i, i, i, ctypes.POINTER(vp), i, vp, vp, sz, vp]
         L.qr_status_string.restype = ctypes.c_char_p
         L.qr_status_string.argtypes = [i]
         _lib = L
@@ -116,4 +118,21 @@ def qr_reduce_compressed(fmt, dtype, ranks, n, packed_out=None, y_out=None, with
            lib().qr_reduce_compressed(_fmt(fmt), _dt(dtype), arr, len(ranks), _dev(packed_out, "packed_out"),
                                       _dev(y_out, "y_out") if y_out is not None else None,
                                       int(n), _stream(stream)))
+    return packed_out, y_out
+
+
+def qr_reduce_compressed_mixed(fmt_in, fmt_out, dtype, ranks, n, packed_out=None, y_out=None,
+                               with_output=True, stream=None):
+    """Inputs packed in fmt_in, re-encoded sum in fmt_out; returns (packed_out, y_out or None)."""
+    dev = ranks[0].device
+    if packed_out is None:
+        packed_out = torch.empty(qr_packed_bytes(fmt_out, n), dtype=torch.uint8, device=dev)
+    if y_out is None and with_output:
+        y_out = torch.empty(n, dtype=dtype, device=dev)
+    arr = (ctypes.c_void_p * len(ranks))(*[_dev(r, "rank").value for r in ranks])
+    _check("qr_reduce_compressed_mixed",
+           lib().qr_reduce_compressed_mixed(_fmt(fmt_in), _fmt(fmt_out), _dt(dtype), arr, len(ranks),
+                                            _dev(packed_out, "packed_out"),
+                                            _dev(y_out, "y_out") if y_out is not None else None,
+                                            int(n), _stream(stream)))
     return packed_out, y_out

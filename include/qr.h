@@ -9,7 +9,8 @@
  * review of arXiv 2412.04964, field key_machinery).  This library provides the
  * three steps as single-GPU calls over buffers resident in device memory:
  * qr_encode (send-side quantization), qr_reduce_compressed (decode R encoded
- * buffers, sum, re-encode, decode) and qr_decode (receive-side dequantization).
+ * buffers, sum, re-encode, decode; qr_reduce_compressed_mixed with separate
+ * input and output formats) and qr_decode (receive-side dequantization).
  *
  * Packed format (one per-rank tile per 2048 values, tiles concatenated):
  *   block  = 32 consecutive values sharing one fp16 scale ("Design Highlights")
@@ -106,6 +107,21 @@ qr_status qr_decode(qr_format fmt, qr_dtype dtype, const void *packed, void *y, 
  * input rank buffers may repeat or overlap each other. */
 qr_status qr_reduce_compressed(qr_format fmt, qr_dtype dtype, const void *const *packed_ranks,
                                int R, void *packed_out, void *y_out, size_t n, void *stream);
+
+/* The same reduction with the inputs in fmt_in and the re-encoded sum (and its
+ * decode) in fmt_out: mixed formats per phase, the "INT6" configuration of the
+ * "Flash Communication" review (fields minor_comments, section 3.2.3, and
+ * forward_implications: INT4 for the reduce-scatter inputs, INT8 for the
+ * all-gather payload).  Any pair of INT3/INT4/INT8 is accepted;
+ * qr_reduce_compressed(f, ...) is qr_reduce_compressed_mixed(f, f, ...).
+ *   packed_ranks  HOST array of R device pointers, qr_packed_bytes(fmt_in, n) each
+ *   packed_out    device, qr_packed_bytes(fmt_out, n) bytes, written
+ *   y_out         device, n values of `dtype`, written, or NULL
+ * Validation and errors as for qr_reduce_compressed (an unknown fmt_in or
+ * fmt_out is QR_ERR_UNSUPPORTED). */
+qr_status qr_reduce_compressed_mixed(qr_format fmt_in, qr_format fmt_out, qr_dtype dtype,
+                                     const void *const *packed_ranks, int R, void *packed_out,
+                                     void *y_out, size_t n, void *stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char *qr_status_string(qr_status s);

@@ -28,7 +28,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert set(names) == {"qr_packed_bytes", "qr_encode", "qr_decode", "qr_reduce_compressed",
-                          "qr_status_string"}
+                          "qr_reduce_compressed_mixed", "qr_status_string"}
     for name in names:
         assert hasattr(L, name), name
 
@@ -120,3 +120,26 @@ def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):
         qa.qr_encode("int4", torch.zeros(2048, dtype=torch.float16), torch.zeros(1152, dtype=torch.uint8))
+
+
+def redm(L, fi=4, fo=8, dt=0, ranks=(A,), R=None, out=B, y=C, n=2048):
+    arr = (ctypes.c_void_p * max(1, len(ranks)))(*ranks)
+    return L.qr_reduce_compressed_mixed(fi, fo, dt, arr, len(ranks) if R is None else R, out, y, n, None)
+
+
+def test_reduce_mixed_validation(L):
+    assert redm(L, fi=5) == qr.QR_ERR_UNSUPPORTED
+    assert redm(L, fo=2) == qr.QR_ERR_UNSUPPORTED
+    assert redm(L, dt=9) == qr.QR_ERR_UNSUPPORTED
+    assert redm(L, R=0) == qr.QR_ERR_ARG
+    assert redm(L, ranks=[A] * 17) == qr.QR_ERR_ARG
+    assert redm(L, n=1000) == qr.QR_ERR_SIZE
+    assert redm(L, out=0) == qr.QR_ERR_ARG
+    assert redm(L, ranks=[A, A + 4]) == qr.QR_ERR_ALIGN
+    # packed_out is sized by fmt_out: an INT8 output (2176 B) starting 2048 B
+    # before the INT4 input (1152 B) overlaps it, an INT3 output (896 B) does not
+    assert redm(L, fi=4, fo=8, out=A - 2048) == qr.QR_ERR_ALIAS
+    assert redm(L, fi=4, fo=8, out=A + 1152 - 16) == qr.QR_ERR_ALIAS
+    assert redm(L, fi=8, fo=3, out=A + 2176 - 16) == qr.QR_ERR_ALIAS
+    assert redm(L, fi=4, fo=3, ranks=[A], out=A - 896, y=0, n=0) == qr.QR_OK
+    assert redm(L, n=0, ranks=[0], out=0, y=0) == qr.QR_OK

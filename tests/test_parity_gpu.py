@@ -208,7 +208,7 @@ def run_pipeline(qa, w, xs):
     packed = [qa.qr_encode(w.fmt, x) for x in xs]
     if not w.reduce:
         return packed, None, qa.qr_decode(w.fmt, packed[0], w.n, w.dtype)
-    out, y = qa.qr_reduce_compressed(w.fmt, w.dtype, packed, w.n)
+    out, y = qa.qr_reduce_compressed_mixed(w.fmt, w.out_fmt, w.dtype, packed, w.n)
     return packed, out, y
 
 
@@ -225,8 +225,11 @@ def check_tiles(oracle, w, xs_host_tiles, packed, out, y, tiles):
     if out is None:
         assert np.array_equal(y[idx_v], oracle.decode(bits, w.io_dtype, wr[0], nt))
         return
-    wout, wy = oracle.reduce(bits, w.io_dtype, wr, nt)
-    assert np.array_equal(out[idx_b], wout), "re-encoded sum differs"
+    obits = BITS[w.out_fmt]
+    otb = P.tile_bytes(obits)
+    idx_o = np.concatenate([np.arange(t * otb, (t + 1) * otb) for t in tiles])
+    wout, wy = oracle.reduce_mixed(bits, obits, w.io_dtype, wr, nt)
+    assert np.array_equal(out[idx_o], wout), "re-encoded sum differs"
     assert np.array_equal(y[idx_v], wy), "decoded sum differs"
 
 
@@ -255,7 +258,7 @@ def test_workload_full_size_sampled(qa, oracle, name):
     if out is not None:
         assert torch.equal(out, out2)
         # the fused final decode equals the standalone decode of the re-encoded sum
-        yd = qa.qr_decode(w.fmt, out, w.n, w.dtype)
+        yd = qa.qr_decode(w.out_fmt, out, w.n, w.dtype)
         assert torch.equal(y.view(torch.int16), yd.view(torch.int16))
     ntiles = w.n // 2048
     rng = np.random.default_rng(ntiles)
@@ -285,3 +288,53 @@ def test_block_scale_every_fp16_scale():
     log("scale check over all fp16 scales")
     assert L.qr_test_scale_check(counters.data_ptr()) == 0
     assert counters.cpu().tolist() == [0] * 6
+
+
+MIXED = [("int4", "int8"), ("int3", "int4"), ("int3", "int8"), ("int4", "int3"), ("int8", "int3"),
+         ("int8", "int4")]
+
+
+@pytest.mark.parametrize("fi,fo", MIXED)
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("R", [1, 2, 5, 8, 16])
+def test_reduce_mixed_parity(qa, oracle, fi, fo, dtype, R):
+    """Inputs in one format, the re-encoded sum in another ("INT6" = INT4 -> INT8)."""
+    n = 37 * 2048
+    kinds = ["normal", "outliers", "scales", "specials"]
+    xs = [gen(kinds[r % 4], dtype, n, seed=77 * R + r) for r in range(R)]
+    log(f"reduce mixed {fi}->{fo} {dtype} R={R}")
+    packed = [qa.qr_encode(fi, dev(x, DT[dtype])) for x in xs]
+    out, y = qa.qr_reduce_compressed_mixed(fi, fo, DT[dtype], packed, n)
+    out2, _ = qa.qr_reduce_compressed_mixed(fi, fo, DT[dtype], packed, n, with_output=False)
+    torch.cuda.synchronize()
+    assert out.numel() == P.tile_bytes(BITS[fo]) * (n // 2048)
+    wout, wy = oracle.reduce_mixed(BITS[fi], BITS[fo], dtype, [oracle.encode(BITS[fi], dtype, x) for x in xs], n)
+    assert np.array_equal(out.cpu().numpy(), wout)
+    assert np.array_equal(u16(y), wy)
+    assert np.array_equal(out2.cpu().numpy(), wout)
+
+
+def test_empty_calls(qa):
+    """n = 0 through every entry point: nothing is launched, no error."""
+    e16 = torch.empty(0, dtype=torch.float16, device="cuda")
+    e8 = torch.empty(0, dtype=torch.uint8, device="cuda")
+    assert qa.qr_encode("int4", e16, e8).numel() == 0
+    assert qa.qr_decode("int3", e8, 0, torch.float16, y=e16).numel() == 0
+    out, y = qa.qr_reduce_compressed("int8", torch.bfloat16, [e8, e8], 0, packed_out=e8,
+                                     y_out=torch.empty(0, dtype=torch.bfloat16, device="cuda"))
+    out, y = qa.qr_reduce_compressed_mixed("int4", "int8", torch.float16, [e8], 0, packed_out=e8, y_out=e16)
+    torch.cuda.synchronize()
+
+
+def test_misaligned_and_aliased_device_buffers(qa):
+    """Real device buffers with an offset of 2 bytes, and an output inside an
+    input: rejected on the host, nothing is launched."""
+    x = torch.zeros(2048 * 2 + 8, dtype=torch.float16, device="cuda")
+    p = torch.empty(1152 * 2, dtype=torch.uint8, device="cuda")
+    with pytest.raises(qa.QRError) as ei:
+        qa.qr_encode("int4", x[1:2049], p[:1152])
+    assert ei.value.status == 3
+    with pytest.raises(qa.QRError) as ei:
+        qa.qr_reduce_compressed("int4", torch.float16, [p[:1152]], 2048, packed_out=p[:1152], y_out=x[:2048])
+    assert ei.value.status == 5
+    torch.cuda.synchronize()

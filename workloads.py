@@ -19,6 +19,8 @@ tiles):
                            std sigma_c = exp(U[ln 0.01, ln 20]), drawn once per
                            seed and shared by all ranks; values sigma_c * N(0,1)
                            independent per rank.
+  int6_r8_fp16_32x1024x4096  the same inputs with the re-encoded sum in INT8
+                           (INT4 reduce inputs + INT8 gather payload, "INT6").
 
 Random numbers come from torch's seeded generators (Philox on the GPU, the CPU
 generator on the host); each (seed, workload, rank) gets its own stream seed.
@@ -44,6 +46,12 @@ class Workload:
     outlier_mult: float = 50.0
     channel_sigma: tuple = None   # (lo, hi) of the log-uniform channel std, or None
     reduce: bool = True
+    fmt_out: str = None           # format of the re-encoded sum, if it differs from fmt
+    data_key: str = None          # name whose random streams the inputs use (default: name)
+
+    @property
+    def out_fmt(self):
+        return self.fmt_out or self.fmt
 
     @property
     def io_dtype(self):
@@ -70,6 +78,11 @@ WORKLOADS = {
     "int4_r8_fp16_32x1024x4096": Workload("int4_r8_fp16_32x1024x4096", "int4", torch.float16, 8,
                                           32 * 1024 * 4096, (32, 1024, 4096),
                                           channel_sigma=(0.01, 20.0)),
+    # mixed formats per phase ("INT6"): INT4 reduce inputs, INT8 re-encoded sum
+    "int6_r8_fp16_32x1024x4096": Workload("int6_r8_fp16_32x1024x4096", "int4", torch.float16, 8,
+                                          32 * 1024 * 4096, (32, 1024, 4096),
+                                          channel_sigma=(0.01, 20.0), fmt_out="int8",
+                                          data_key="int4_r8_fp16_32x1024x4096"),
 }
 
 BENCH_WORKLOAD = "int4_r8_fp16_32x1024x4096"
@@ -99,14 +112,14 @@ def _gen(device, seed):
 
 def channel_sigmas(w, seed, device="cpu"):
     lo, hi = w.channel_sigma
-    g = _gen(device, derive_seed(seed, w.name, "channels"))
+    g = _gen(device, derive_seed(seed, w.data_key or w.name, "channels"))
     u = torch.rand(w.shape[-1], generator=g, device=device, dtype=torch.float32)
     return torch.exp(math.log(lo) + u * (math.log(hi) - math.log(lo)))
 
 
 def rank_input(w, rank, seed=0, device="cpu"):
     """Rank `rank`'s input: a flat tensor of w.n values of w.dtype on `device`."""
-    g = _gen(device, derive_seed(seed, w.name, rank))
+    g = _gen(device, derive_seed(seed, w.data_key or w.name, rank))
     x = torch.randn(w.n, generator=g, device=device, dtype=torch.float32)
     if w.channel_sigma is not None:
         x.view(-1, w.shape[-1]).mul_(channel_sigmas(w, seed, device))
