@@ -19,7 +19,7 @@ import numpy as np
 
 from . import build as _build
 
-FMT_BITS = {"int3": 3, "int4": 4, "int8": 8}
+FMT_BITS = {"int3": 3, "int4": 4, "int8": 8, "asym4": 20, "asym8": 24}
 DTYPES = {"fp16": 0, "bf16": 1}
 TILE = 2048
 BLOCK = 32
@@ -65,6 +65,9 @@ class Oracle:
         L.qro_reduce_mixed.restype = ctypes.c_int
         L.qro_reduce_mixed.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(_u8p),
                                        ctypes.c_int, _u8p, _u16p, ctypes.c_size_t]
+        L.qro_group_params.restype = None
+        L.qro_group_params.argtypes = [ctypes.c_int, ctypes.c_float, ctypes.c_float, _u16p, _f32p,
+                                       ctypes.POINTER(ctypes.c_int)]
         L.qro_block_scale.restype = None
         L.qro_block_scale.argtypes = [ctypes.c_int, ctypes.c_float, _u16p, _f32p]
         L.qro_f16_to_f32.restype = ctypes.c_float
@@ -141,6 +144,14 @@ class Oracle:
         e = ctypes.c_float()
         self.L.qro_block_scale(int(bits), float(m), ctypes.byref(d), ctypes.byref(e))
         return d.value, e.value
+
+    def group_params(self, bits, lo, hi):
+        d = ctypes.c_uint16()
+        e = ctypes.c_float()
+        z = ctypes.c_int()
+        self.L.qro_group_params(int(bits), float(lo), float(hi), ctypes.byref(d), ctypes.byref(e),
+                                ctypes.byref(z))
+        return d.value, e.value, z.value
 
     def _conv(self, fn, x, in_t, out_t, in_p, out_p):
         x = np.ascontiguousarray(x, dtype=in_t).ravel()

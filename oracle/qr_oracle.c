@@ -44,6 +44,16 @@
  *  R6  the reduction decodes each rank exactly into fp32, sums in fixed rank
  *      order 0..R-1 starting from rank 0's value, rounds the sum to the I/O
  *      dtype, re-encodes it, and decodes that re-encoded tile.
+ *  R7  asymmetric group codec ([FC] pith_summary / key_machinery: asymmetric
+ *      quantization with group size 128, a scale and a zero point per group;
+ *      minor_comments on Algorithm 1: dequantize as (q - z) * s): a group is
+ *      128 consecutive values; its range [lo, hi] always includes 0 (lo =
+ *      min(min x, 0), hi = max(max x, 0)); s = fp16_RNE(min(RN32(RN32(hi - lo)
+ *      / (2^b - 1)), 65504)); e = RN32(1 / s) (0 when s == 0); z =
+ *      clamp(rint(RN32(-lo * e)), 0, 2^b - 1); q = clamp(rint(RN32(x * e)) + z,
+ *      0, 2^b - 1); decode (q - z) * s, exact in fp32.  A tile of 2048 values
+ *      is [codes (as INT4 / INT8) | 16 fp16 scales | 16 uint8 zero points]:
+ *      1072 bytes for 4-bit codes, 2096 for 8-bit.
  *
  * All floating point is IEEE binary32 with round-to-nearest-even; build with
  * -O2 -ffp-contract=off and without -ffast-math.
@@ -145,12 +155,32 @@ static uint16_t f32_to_dtype(int dtype, float x) {
 /* tile layout (R1, R5)                                                      */
 /* ------------------------------------------------------------------------ */
 
-static int fmt_bits(int fmt) { return (fmt == 3 || fmt == 4 || fmt == 8) ? fmt : 0; }
+/* Format ids: 3, 4, 8 = symmetric block codec with that many bits; 20, 24 =
+   asymmetric group codec with 4 or 8 bits (R7). */
+#define QRO_ASYM 16
+static int fmt_bits(int fmt) {
+  if (fmt == 3 || fmt == 4 || fmt == 8) return fmt;
+  if (fmt == QRO_ASYM + 4 || fmt == QRO_ASYM + 8) return fmt - QRO_ASYM;
+  return 0;
+}
+static int fmt_asym(int fmt) { return fmt > QRO_ASYM; }
+
+#define QRO_AGROUP 128 /* values per asymmetric group (R7) */
+#define QRO_AGROUPS (QRO_TILE / QRO_AGROUP)
 
 /* Bytes of one tile: code planes plus 64 binary16 scales. */
 static size_t tile_bytes(int bits) {
   size_t code_bits = (size_t)QRO_TILE * (size_t)bits;
   return code_bits / 8 + 2 * QRO_BLOCKS;
+}
+
+/* Asymmetric tile: codes plus 16 binary16 scales and 16 uint8 zero points. */
+static size_t asym_tile_bytes(int bits) {
+  return (size_t)QRO_TILE * (size_t)bits / 8 + 3 * QRO_AGROUPS;
+}
+
+static size_t fmt_tile_bytes(int fmt) {
+  return fmt_asym(fmt) ? asym_tile_bytes(fmt_bits(fmt)) : tile_bytes(fmt_bits(fmt));
 }
 
 /* Byte offset of the scale region inside a tile. */
@@ -159,7 +189,7 @@ static size_t scale_offset(int bits) { return (size_t)QRO_TILE * (size_t)bits / 
 size_t qro_packed_bytes(int fmt, size_t n) {
   int bits = fmt_bits(fmt);
   if (!bits || n % QRO_TILE) return 0;
-  return n / QRO_TILE * tile_bytes(bits);
+  return n / QRO_TILE * fmt_tile_bytes(fmt);
 }
 
 /* INT3: the 2-bit plane is 256 little-endian uint16 words (word u holds the
@@ -273,6 +303,82 @@ static void encode_tile(int bits, const float *x, uint8_t *tile) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* asymmetric group codec (R7)                                              */
+/* ------------------------------------------------------------------------ */
+
+static size_t asym_scale_offset(int bits) { return (size_t)QRO_TILE * (size_t)bits / 8; }
+static size_t asym_zero_offset(int bits) { return asym_scale_offset(bits) + 2 * QRO_AGROUPS; }
+
+/* Scale, multiplier and zero point of a group with range [lo, hi] (lo <= 0 <= hi). */
+void qro_group_params(int bits, float lo, float hi, uint16_t *d_bits, float *e, int *z) {
+  const int qmax = (1 << bits) - 1;
+  float t = (hi - lo) / (float)qmax;
+  if (t > 65504.0f) t = 65504.0f; /* saturate the group scale */
+  *d_bits = qro_f32_to_f16(t);
+  float d = qro_f16_to_f32(*d_bits);
+  *e = (d == 0.0f) ? 0.0f : 1.0f / d; /* group multiplier */
+  float zf = rintf(-lo * *e);
+  zf = fminf(fmaxf(zf, 0.0f), (float)qmax);
+  *z = (int)zf;
+}
+
+static void encode_group_asym(int bits, const float x[QRO_AGROUP], unsigned codes[QRO_AGROUP],
+                              uint16_t *d_bits, int *z) {
+  const int qmax = (1 << bits) - 1;
+  float lo = 0.0f, hi = 0.0f; /* the range always includes 0 */
+  for (int i = 0; i < QRO_AGROUP; ++i) {
+    if (x[i] < lo) lo = x[i];
+    if (x[i] > hi) hi = x[i];
+  }
+  float e;
+  qro_group_params(bits, lo, hi, d_bits, &e, z);
+  for (int i = 0; i < QRO_AGROUP; ++i) {
+    float u = x[i] * e;
+    long k = lrintf(u) + *z;
+    if (k < 0) k = 0;
+    if (k > qmax) k = qmax;
+    codes[i] = (unsigned)k;
+  }
+}
+
+static void encode_tile_asym(int bits, const float *x, uint8_t *tile) {
+  memset(tile, 0, asym_tile_bytes(bits));
+  for (int g = 0; g < QRO_AGROUPS; ++g) {
+    unsigned codes[QRO_AGROUP];
+    uint16_t d_bits;
+    int z;
+    encode_group_asym(bits, x + g * QRO_AGROUP, codes, &d_bits, &z);
+    for (int i = 0; i < QRO_AGROUP; ++i) put_code(bits, tile, g * QRO_AGROUP + i, codes[i]);
+    uint8_t *p = tile + asym_scale_offset(bits) + 2 * g;
+    p[0] = (uint8_t)(d_bits & 0xff);
+    p[1] = (uint8_t)(d_bits >> 8);
+    tile[asym_zero_offset(bits) + g] = (uint8_t)z;
+  }
+}
+
+/* Algorithm 1 of the Flash Communication paper as the review describes it:
+   (q - z) * s, exact in fp32 (|q - z| < 2^8, s has 11 significant bits). */
+static float decode_value_asym(int bits, const uint8_t *tile, int i) {
+  int g = i / QRO_AGROUP;
+  const uint8_t *p = tile + asym_scale_offset(bits) + 2 * g;
+  float d = qro_f16_to_f32((uint16_t)(p[0] | (p[1] << 8)));
+  int z = tile[asym_zero_offset(bits) + g];
+  return (float)((int)get_code(bits, tile, i) - z) * d;
+}
+
+/* Format-generic tile encode / value decode. */
+static void encode_tile_fmt(int fmt, const float *x, uint8_t *tile) {
+  if (fmt_asym(fmt))
+    encode_tile_asym(fmt_bits(fmt), x, tile);
+  else
+    encode_tile(fmt_bits(fmt), x, tile);
+}
+
+static float decode_value_fmt(int fmt, const uint8_t *tile, int i) {
+  return fmt_asym(fmt) ? decode_value_asym(fmt_bits(fmt), tile, i) : decode_value(fmt_bits(fmt), tile, i);
+}
+
+/* ------------------------------------------------------------------------ */
 /* exported entry points                                                     */
 /* ------------------------------------------------------------------------ */
 
@@ -285,12 +391,11 @@ static int check(int fmt, int dtype, size_t n) {
 
 int qro_encode(int fmt, int dtype, const uint16_t *x, uint8_t *packed, size_t n) {
   if (check(fmt, dtype, n)) return -1;
-  int bits = fmt_bits(fmt);
-  size_t tb = tile_bytes(bits);
+  size_t tb = fmt_tile_bytes(fmt);
   float xf[QRO_TILE];
   for (size_t t = 0; t < n / QRO_TILE; ++t) {
     for (int i = 0; i < QRO_TILE; ++i) xf[i] = dtype_to_f32(dtype, x[t * QRO_TILE + i]);
-    encode_tile(bits, xf, packed + t * tb);
+    encode_tile_fmt(fmt, xf, packed + t * tb);
   }
   return 0;
 }
@@ -298,20 +403,18 @@ int qro_encode(int fmt, int dtype, const uint16_t *x, uint8_t *packed, size_t n)
 /* Exact binary32 decode (before any rounding to the I/O dtype). */
 int qro_decode_f32(int fmt, const uint8_t *packed, float *y, size_t n) {
   if (check(fmt, QRO_FP16, n)) return -1;
-  int bits = fmt_bits(fmt);
-  size_t tb = tile_bytes(bits);
+  size_t tb = fmt_tile_bytes(fmt);
   for (size_t t = 0; t < n / QRO_TILE; ++t)
-    for (int i = 0; i < QRO_TILE; ++i) y[t * QRO_TILE + i] = decode_value(bits, packed + t * tb, i);
+    for (int i = 0; i < QRO_TILE; ++i) y[t * QRO_TILE + i] = decode_value_fmt(fmt, packed + t * tb, i);
   return 0;
 }
 
 int qro_decode(int fmt, int dtype, const uint8_t *packed, uint16_t *y, size_t n) {
   if (check(fmt, dtype, n)) return -1;
-  int bits = fmt_bits(fmt);
-  size_t tb = tile_bytes(bits);
+  size_t tb = fmt_tile_bytes(fmt);
   for (size_t t = 0; t < n / QRO_TILE; ++t)
     for (int i = 0; i < QRO_TILE; ++i)
-      y[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value(bits, packed + t * tb, i));
+      y[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value_fmt(fmt, packed + t * tb, i));
   return 0;
 }
 
@@ -324,20 +427,19 @@ int qro_decode(int fmt, int dtype, const uint8_t *packed, uint16_t *y, size_t n)
 int qro_reduce_mixed(int fmt_in, int fmt_out, int dtype, const uint8_t *const *ranks, int R,
                      uint8_t *packed_out, uint16_t *y_out, size_t n) {
   if (check(fmt_in, dtype, n) || check(fmt_out, dtype, n) || R < 1) return -1;
-  int bits = fmt_bits(fmt_in), obits = fmt_bits(fmt_out);
-  size_t tb = tile_bytes(bits), otb = tile_bytes(obits);
+  size_t tb = fmt_tile_bytes(fmt_in), otb = fmt_tile_bytes(fmt_out);
   float z[QRO_TILE];
   for (size_t t = 0; t < n / QRO_TILE; ++t) {
     for (int i = 0; i < QRO_TILE; ++i) {
-      float s = decode_value(bits, ranks[0] + t * tb, i);
-      for (int r = 1; r < R; ++r) s = s + decode_value(bits, ranks[r] + t * tb, i);
+      float s = decode_value_fmt(fmt_in, ranks[0] + t * tb, i);
+      for (int r = 1; r < R; ++r) s = s + decode_value_fmt(fmt_in, ranks[r] + t * tb, i);
       z[i] = dtype_to_f32(dtype, f32_to_dtype(dtype, s));
     }
     uint8_t *out = packed_out + t * otb;
-    encode_tile(obits, z, out);
+    encode_tile_fmt(fmt_out, z, out);
     if (y_out)
       for (int i = 0; i < QRO_TILE; ++i)
-        y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value(obits, out, i));
+        y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value_fmt(fmt_out, out, i));
   }
   return 0;
 }

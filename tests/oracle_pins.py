@@ -704,6 +704,278 @@ def pin_reduce_mixed_exact(o, seed=10):
 
 
 # ---------------------------------------------------------------------------
+# asymmetric group-128 codec (scale + zero point per 128 values)
+# ---------------------------------------------------------------------------
+
+ASYM = {4: 20, 8: 24}   # bits -> format id
+AGROUP = 128
+
+
+def asym_tile_bytes(bits):
+    return TILE * bits // 8 + 3 * (TILE // AGROUP)
+
+
+def asym_unpack(bits, packed):
+    """Codes (T, 2048), scale bits (T, 16), zero points (T, 16) of asymmetric tiles."""
+    t = np.asarray(packed, np.uint8).reshape(-1, asym_tile_bytes(bits))
+    cb = TILE * bits // 8
+    if bits == 8:
+        codes = t[:, :2048].astype(np.int64)
+    else:
+        words = t[:, :1024].copy().view("<u4").astype(np.int64)
+        codes = ((words[:, :, None] >> (4 * np.arange(8))) & 15).reshape(-1, 2048)
+    scales = t[:, cb:cb + 32].copy().view("<u2")
+    zeros = t[:, cb + 32:cb + 48].astype(np.int64)
+    return codes, scales, zeros
+
+
+def asym_pack(bits, codes, scale_bits, zeros):
+    codes = np.asarray(codes, np.int64).reshape(-1, 2048)
+    T = codes.shape[0]
+    out = np.zeros((T, asym_tile_bytes(bits)), np.uint8)
+    cb = TILE * bits // 8
+    if bits == 8:
+        out[:, :2048] = codes
+    else:
+        c = codes.reshape(T, 256, 8)
+        words = np.zeros((T, 256), np.uint32)
+        for j in range(8):
+            words |= (c[:, :, j] << (4 * j)).astype(np.uint32)
+        out[:, :1024] = words.view(np.uint8).reshape(T, 1024)
+    out[:, cb:cb + 32] = np.asarray(scale_bits, np.uint16).reshape(T, 16).view(np.uint8).reshape(T, 32)
+    out[:, cb + 32:cb + 48] = np.asarray(zeros, np.uint8).reshape(T, 16)
+    return out.ravel()
+
+
+def pin_asym_tile_layout(o):
+    for bits, fid in ASYM.items():
+        assert o.packed_bytes(fid, 2048) == asym_tile_bytes(bits) == (1072 if bits == 4 else 2096)
+        assert o.packed_bytes(fid, 2048 * 5) == 5 * asym_tile_bytes(bits)
+        assert o.packed_bytes(fid, 100) == 0
+        # codes in the symmetric layout, group scale / zero point at their slots
+        x = np.zeros(TILE)
+        x[:8] = np.arange(8) - 3.0          # group 0: range [-3, 4]
+        x[AGROUP * 5] = 6.0                 # group 5: range [0, 6]
+        p = o.encode(fid, "fp16", f16_bits(x))
+        codes, sb, zp = asym_unpack(bits, p)
+        qmax = (1 << bits) - 1
+        assert f16_value(sb[0, 0]) == np.float16(7.0 / qmax) and zp[0, 5] == 0
+        assert f16_value(sb[0, 5]) == np.float16(6.0 / qmax)
+        assert np.all(sb[0, [1, 2, 3, 4] + list(range(6, 16))] == 0) and np.all(zp[0, 1:] == 0)
+
+
+def _asym_exact_groups(rng, bits, dtype, ng):
+    """Groups of values (k - z) * s with k in [0, qmax], both ends present."""
+    qmax = (1 << bits) - 1
+    sig = 11 if dtype == "fp16" else 8
+    kk = rng.integers(0, qmax + 1, size=(ng, AGROUP))
+    kk[:, 0] = 0
+    kk[:, 1] = qmax
+    z = rng.integers(0, qmax + 1, size=ng)
+    s = []
+    for g in range(ng):
+        m = 3 if (bits == 4 and sig == 11 and g % 2) else 1
+        s.append(m * 2.0 ** int(rng.integers(-12, 3)))
+    s = np.array(s)
+    x = (kk - z[:, None]) * s[:, None]
+    return kk, z, s, x
+
+
+def pin_asym_exact_roundtrip(o, seed=21):
+    rng = np.random.default_rng(seed)
+    for bits, fid in ASYM.items():
+        for dtype in DTYPES:
+            ng = 16 * 6
+            kk, z, s, x = _asym_exact_groups(rng, bits, dtype, ng)
+            xb = dtype_bits(dtype, x.ravel())
+            p = o.encode(fid, dtype, xb)
+            codes, sb, zp = asym_unpack(bits, p)
+            assert np.array_equal(codes.reshape(ng, AGROUP), kk), (bits, dtype)
+            assert np.array_equal(zp.ravel(), z), (bits, dtype)
+            assert np.array_equal(sb.ravel(), f16_bits(s)), (bits, dtype)
+            assert np.array_equal(o.decode(fid, dtype, p, x.size), xb), (bits, dtype)
+
+
+def pin_asym_bruteforce_pow2(o):
+    """Groups [-z*2^m, (qmax-z)*2^m, x, 0...]: scale 2^m, zero point z, and the
+    code of x is clamp(round_half_even(x / 2^m) + z, 0, qmax) (float64)."""
+    allb, allv = all_finite("fp16")
+    for bits, fid in ASYM.items():
+        qmax = (1 << bits) - 1
+        for m, z in ((-14, 0), (-6, 3), (0, qmax // 2), (2, qmax), (-20, 1)):
+            lo, hi = -z * 2.0 ** m, (qmax - z) * 2.0 ** m
+            sel = (allv >= lo) & (allv <= hi)
+            xb, xv = allb[sel], allv[sel]
+            nb = xb.size
+            groups = np.zeros((nb, AGROUP), np.uint16)
+            groups[:, 0] = f16_bits(lo)
+            groups[:, 1] = f16_bits(hi)
+            groups[:, 2] = xb
+            ng = -(-nb // 16) * 16
+            buf = np.zeros((ng, AGROUP), np.uint16)
+            buf[:nb] = groups
+            p = o.encode(fid, "fp16", buf.ravel())
+            codes, sb, zp = asym_unpack(bits, p)
+            codes = codes.reshape(-1, AGROUP)[:nb]
+            want = np.clip(np.rint(xv / 2.0 ** m) + z, 0, qmax)
+            bad = codes[:, 2] != want
+            assert not bad.any(), (bits, m, z, xv[bad][:4], codes[bad, 2][:4], want[bad][:4])
+            assert np.all(zp.ravel()[:nb] == z) and np.all(sb.ravel()[:nb] == pow2_f16_bits(m))
+
+
+def pin_asym_bruteforce_general_scale(o):
+    """Groups [-z*d, (qmax-z)*d, x, 0...] with d a non-power-of-two fp16 scale
+    (both ends exact in fp16, so the range divided by qmax is d exactly) and
+    every finite fp16 x in the range: scale d, zero point z, and the code of x
+    is clamp(round_half_even(RN32(x * RN32(1/d))) + z, 0, qmax), the products
+    formed in float64 and rounded once.  For the scales 0x0F80 and 0x3300 some
+    x round differently under x / d, so the check also tells "multiply by the
+    fp32 reciprocal" from "divide by the scale"."""
+    allb, allv = all_finite("fp16")
+    for bits, fid in ASYM.items():
+        qmax = (1 << bits) - 1
+        diff_seen = 0
+        for d_bits in (0x0F80, 0x3300, 0x0F90, 0x3A00):
+            d = float(f16_value(np.uint16(d_bits)))
+            for z in (0, qmax, (qmax + 1) // 2, 3):
+                lo, hi = -z * d, (qmax - z) * d
+                if f16_value(f16_bits(lo)) != lo or f16_value(f16_bits(hi)) != hi:
+                    continue
+                sel = (allv >= lo) & (allv <= hi)
+                xb, xv = allb[sel], allv[sel]
+                nb = xb.size
+                ng = -(-nb // 16) * 16
+                buf = np.zeros((ng, AGROUP), np.uint16)
+                buf[:nb, 0] = f16_bits(lo)
+                buf[:nb, 1] = f16_bits(hi)
+                buf[:nb, 2] = xb
+                p = o.encode(fid, "fp16", buf.ravel())
+                codes, sb, zp = asym_unpack(bits, p)
+                codes = codes.reshape(-1, AGROUP)[:nb]
+                assert np.all(sb.ravel()[:nb] == d_bits) and np.all(zp.ravel()[:nb] == z), (bits, hex(d_bits), z)
+                e = np.float64(np.float32(1.0 / d))
+                want = np.clip(np.rint((xv * e).astype(np.float32).astype(np.float64)) + z, 0, qmax)
+                bad = codes[:, 2] != want
+                assert not bad.any(), (bits, hex(d_bits), z, xv[bad][:4], codes[bad, 2][:4], want[bad][:4])
+                by_div = np.clip(np.rint((xv / d).astype(np.float32).astype(np.float64)) + z, 0, qmax)
+                diff_seen += int((by_div != want).sum())
+        assert diff_seen > 0, bits
+
+
+def pin_asym_group_params(o):
+    """Every positive finite fp16 scale s and a zero point z: a group range
+    [-z*s, (qmax-z)*s] gives scale s, multiplier RN32(1/s) (float64 quotient
+    rounded once), zero point z."""
+    d_bits = np.arange(1, 0x7C00, 7, dtype=np.uint16)
+    d = f16_value(d_bits)
+    for bits in (4, 8):
+        qmax = (1 << bits) - 1
+        for i in range(d_bits.size):
+            z = (i * 5) % (qmax + 1)
+            lo, hi = np.float32(-z * d[i]), np.float32((qmax - z) * d[i])
+            if float(hi) - float(lo) != qmax * d[i] or qmax * d[i] > 65504 * qmax:
+                continue
+            db, e, zz = o.group_params(bits, lo, hi)
+            assert db == d_bits[i] and e == np.float32(1.0 / d[i]) and zz == z, (bits, hex(int(d_bits[i])), z)
+        assert o.group_params(bits, 0.0, 0.0) == (0, 0.0, 0)
+        db, e, zz = o.group_params(bits, -1e30, 1e30)
+        assert db == 0x7BFF
+
+
+def pin_asym_special_groups(o):
+    for bits, fid in ASYM.items():
+        qmax = (1 << bits) - 1
+        for dtype in DTYPES:
+            x = np.zeros(TILE)
+            x[AGROUP:2 * AGROUP] = 0.5                       # positive only: lo = 0 -> z = 0, all codes qmax
+            x[2 * AGROUP:3 * AGROUP] = -0.25                 # negative only: hi = 0 -> z = qmax, codes 0
+            x[3 * AGROUP:4 * AGROUP:2] = -0.0                # zeros and -0
+            p = o.encode(fid, dtype, dtype_bits(dtype, x))
+            codes, sb, zp = asym_unpack(bits, p)
+            c = codes.reshape(16, AGROUP)
+            assert sb[0, 0] == 0 and zp[0, 0] == 0 and np.all(c[0] == 0)
+            assert zp[0, 1] == 0 and np.all(c[1] == qmax)
+            assert zp[0, 2] == qmax and np.all(c[2] == 0)
+            assert sb[0, 3] == 0 and np.all(c[3] == 0)
+            y = dtype_value(dtype, o.decode(fid, dtype, p, TILE))
+            assert np.all(y[:AGROUP] == 0) and np.all(y[3 * AGROUP:4 * AGROUP] == 0)
+            assert np.all(np.abs(y[AGROUP:2 * AGROUP] - 0.5) <= 0.5 / qmax)
+
+
+def pin_asym_decode_algorithm1(o, seed=22):
+    """Decode = dtype_RNE((q - z) * s) for arbitrary codes, scales and zero points."""
+    rng = np.random.default_rng(seed)
+    for bits, fid in ASYM.items():
+        T = 3
+        codes = rng.integers(0, 1 << bits, size=(T, 2048))
+        sb = rng.integers(0, 0x7C00, size=(T, 16)).astype(np.uint16)
+        zp = rng.integers(0, 1 << bits, size=(T, 16))
+        p = asym_pack(bits, codes, sb, zp)
+        exact = ((codes.reshape(T, 16, AGROUP) - zp[:, :, None]) * f16_value(sb)[:, :, None]).ravel()
+        assert np.array_equal(o.decode_f32(fid, p, T * 2048).astype(np.float64), exact), bits
+        for dtype in DTYPES:
+            want = f16_bits(exact) if dtype == "fp16" else bf16_bits(exact)
+            assert np.array_equal(o.decode(fid, dtype, p, T * 2048), want), (bits, dtype)
+
+
+def pin_asym_reduce_exact(o, seed=23):
+    """Two ranks on the same group grid (scale s, zero point z) whose sums stay
+    on it and reach both ends: the re-encoded sum has scale s and zero point z
+    and decodes to the exact sum; also the 4-bit -> 8-bit mixed case."""
+    rng = np.random.default_rng(seed)
+    for bits, fid in ASYM.items():
+        qmax = (1 << bits) - 1
+        z = (qmax + 1) // 2
+        for dtype in DTYPES:
+            ng = 32
+            a = rng.integers(-z, qmax - z + 1, size=(ng, AGROUP))
+            b = np.clip(rng.integers(-3, 4, size=(ng, AGROUP)), -z - a, qmax - z - a)
+            a[:, :4] = [-z, qmax - z, 0, 0]
+            b[:, :4] = [0, 0, -z, qmax - z]
+            tot = a + b
+            assert np.all((tot >= -z) & (tot <= qmax - z))
+            s = 2.0 ** rng.integers(-6, 2, size=ng)
+            ra = o.encode(fid, dtype, dtype_bits(dtype, (a * s[:, None]).ravel()))
+            rb = o.encode(fid, dtype, dtype_bits(dtype, (b * s[:, None]).ravel()))
+            out, y = o.reduce(fid, dtype, [ra, rb], ng * AGROUP)
+            codes, sb, zp = asym_unpack(bits, out)
+            assert np.array_equal(sb.ravel(), f16_bits(s)) and np.all(zp == z), (bits, dtype)
+            assert np.array_equal(codes.reshape(ng, AGROUP), tot + z), (bits, dtype)
+            assert np.array_equal(y, dtype_bits(dtype, (tot * s[:, None]).ravel())), (bits, dtype)
+            if bits == 4:   # same inputs re-encoded with 8-bit codes: scale s*15/255, exact when representable
+                out8, y8 = o.reduce_mixed(fid, ASYM[8], dtype, [ra, rb], ng * AGROUP)
+                c8, s8, z8 = asym_unpack(8, out8)
+                d8 = f16_value(f16_bits(s * 15 / 255))
+                assert np.array_equal(s8.ravel(), f16_bits(s * 15 / 255)), dtype
+                assert np.all(np.abs(dtype_value(dtype, y8) - (tot * s[:, None]).ravel())
+                              <= np.repeat(d8, AGROUP) * 0.51 + np.abs((tot * s[:, None]).ravel()) * 2.0 ** -7)
+
+
+def pin_asym_error_bound(o, seed=24):
+    """|decode(encode(x)) - x| <= (0.5 + qmax * 2^-11) * s for every value: inside
+    the grid the error is half a step; the fp16 rounding of the scale can leave
+    the grid's top end short of the group maximum by up to qmax * 2^-11 steps,
+    where the value clamps.  And the bound is not vacuous."""
+    rng = np.random.default_rng(seed)
+    for bits, fid in ASYM.items():
+        for dtype in DTYPES:
+            ng = 16 * 8
+            x = rng.standard_normal((ng, AGROUP)) * np.exp(rng.uniform(-4, 4, (ng, 1))) + \
+                rng.uniform(-2, 2, (ng, 1))
+            xb = dtype_bits(dtype, x.astype(np.float32).astype(np.float64).ravel()) if dtype == "bf16" \
+                else f16_bits(x.ravel())
+            xv = dtype_value(dtype, xb)
+            p = o.encode(fid, dtype, xb)
+            y = o.decode_f32(fid, p, xv.size).astype(np.float64)
+            _, sb, _ = asym_unpack(bits, p)
+            s = np.repeat(f16_value(sb.ravel()), AGROUP)
+            err = np.abs(y - xv)
+            qmax = (1 << bits) - 1
+            assert np.all(err <= (0.5 + qmax * 2.0 ** -11 + 1e-3) * s + 1e-30), (bits, dtype, (err / s).max())
+            assert np.median(err / s) < 0.35
+
+
+# ---------------------------------------------------------------------------
 # P8: error bound of encode -> reduce -> decode against the exact sum
 # ---------------------------------------------------------------------------
 
@@ -745,6 +1017,34 @@ def pin_error_bound(o, seed=8):
                 assert np.median(err / bound) < 0.6
 
 
+
+def pin_asym_zero_point_clamp(o):
+    """The zero point is clamped to [0, 2^b - 1] where rounding of the scale
+    pushes -lo / s past the top code.  Hand-derived cases:
+      * fp16, range [-k * 2^-24, 0] with k = 22 (4-bit) or 357 (8-bit):
+        t = k / qmax * 2^-24 rounds to the smallest subnormal 2^-24 (ratio 1.47,
+        1.40 < 1.5), so -lo / s = k > qmax and z = qmax; the minimum then
+        clamps to code 0 and zeros encode as z.
+      * bf16, range [-2^30, 0]: t = 2^30 / qmax > 65504 saturates the scale
+        at 65504 (0x7BFF), -lo / s = 2^30 / 65504 > 16000 and z = qmax."""
+    for bits, fid in ASYM.items():
+        qmax = (1 << bits) - 1
+        k = 22 if bits == 4 else 357
+        cases = [("fp16", -k * 2.0 ** -24, 0x0001), ("bf16", -2.0 ** 30, 0x7BFF)]
+        for dtype, lo, want_sb in cases:
+            x = np.zeros(TILE)
+            x[0] = lo
+            p = o.encode(fid, dtype, dtype_bits(dtype, x))
+            codes, sb, zp = asym_unpack(bits, p)
+            assert sb[0, 0] == want_sb and zp[0, 0] == qmax, (bits, dtype, sb[0, 0], zp[0, 0])
+            assert codes[0, 0] == 0 and np.all(codes[0, 1:AGROUP] == qmax), (bits, dtype)
+            y = dtype_value(dtype, o.decode(fid, dtype, p, TILE))
+            assert np.all(y[1:] == 0), (bits, dtype)
+            want = -qmax * float(f16_value(np.uint16(want_sb)))   # exact, then rounded to the dtype
+            assert y[0] == dtype_value(dtype, dtype_bits(dtype, np.array([want])))[0], (bits, dtype)
+
+
+
 ALL_PINS = [
     pin_tile_bytes,
     pin_unit_bit_order,
@@ -764,5 +1064,16 @@ ALL_PINS = [
     pin_reduce_exact_terms,
     pin_reduce_mixed_r1_composition,
     pin_reduce_mixed_exact,
+    pin_asym_tile_layout,
+    pin_asym_exact_roundtrip,
+    pin_asym_bruteforce_pow2,
+    pin_asym_bruteforce_general_scale,
+    pin_asym_group_params,
+    pin_asym_special_groups,
+    pin_asym_decode_algorithm1,
+    pin_asym_reduce_exact,
+    pin_asym_zero_point_clamp,
+    pin_asym_error_bound,
     pin_error_bound,
 ]
+

@@ -51,30 +51,31 @@ MUTANTS = [
         ("p[0] = (uint8_t)(d & 0xff);\n  p[1] = (uint8_t)(d >> 8);",
          "p[1] = (uint8_t)(d & 0xff);\n  p[0] = (uint8_t)(d >> 8);"),
         ("return (uint16_t)(p[0] | (p[1] << 8));", "return (uint16_t)(p[1] | (p[0] << 8));")]),
-    ("scale not saturated at 65504", [("if (t > 65504.0f) t = 65504.0f;", "")]),
-    ("multiplier rounded to fp16", [("*e = (d == 0.0f) ? 0.0f : 1.0f / d;",
-                                     "*e = (d == 0.0f) ? 0.0f : qro_f16_to_f32(qro_f32_to_f16(1.0f / d));")]),
-    ("multiplier from the block maximum", [("*e = (d == 0.0f) ? 0.0f : 1.0f / d;",
-                                            "*e = (d == 0.0f) ? 0.0f : (float)Q / m;")]),
+    ("scale not saturated at 65504", [("if (t > 65504.0f) t = 65504.0f; /* largest finite binary16 */", "")]),
+    ("multiplier rounded to fp16", [("*e = (d == 0.0f) ? 0.0f : 1.0f / d;\n}",
+                                     "*e = (d == 0.0f) ? 0.0f : qro_f16_to_f32(qro_f32_to_f16(1.0f / d));\n}")]),
+    ("multiplier from the block maximum", [("*e = (d == 0.0f) ? 0.0f : 1.0f / d;\n}",
+                                            "*e = (d == 0.0f) ? 0.0f : (float)Q / m;\n}")]),
     ("divide by the scale", [("float v = x[i] * e;",
                               "float v = (e == 0.0f) ? 0.0f : x[i] / qro_f16_to_f32(*d_bits);")]),
     ("signed maximum", [("float a = fabsf(x[i]);", "float a = x[i];")]),
     ("decode bias dropped", [("return (float)((int)code - Q) * d;", "return (float)((int)code - Q + 1) * d;")]),
     ("decode sign flipped", [("return (float)((int)code - Q) * d;", "return (float)(Q - (int)code) * d;")]),
     ("rank order reversed", [
-        ("float s = decode_value(bits, ranks[0] + t * tb, i);\n"
-         "      for (int r = 1; r < R; ++r) s = s + decode_value(bits, ranks[r] + t * tb, i);",
-         "float s = decode_value(bits, ranks[R - 1] + t * tb, i);\n"
-         "      for (int r = R - 2; r >= 0; --r) s = s + decode_value(bits, ranks[r] + t * tb, i);")]),
-    ("rank 0 dropped", [("float s = decode_value(bits, ranks[0] + t * tb, i);", "float s = 0.0f;")]),
+        ("float s = decode_value_fmt(fmt_in, ranks[0] + t * tb, i);\n"
+         "      for (int r = 1; r < R; ++r) s = s + decode_value_fmt(fmt_in, ranks[r] + t * tb, i);",
+         "float s = decode_value_fmt(fmt_in, ranks[R - 1] + t * tb, i);\n"
+         "      for (int r = R - 2; r >= 0; --r) s = s + decode_value_fmt(fmt_in, ranks[r] + t * tb, i);")]),
+    ("rank 0 dropped", [("float s = decode_value_fmt(fmt_in, ranks[0] + t * tb, i);", "float s = 0.0f;")]),
     ("last rank dropped", [("for (int r = 1; r < R; ++r) s = s +", "for (int r = 1; r < R - 1; ++r) s = s +")]),
     ("sum in double", [
-        ("float s = decode_value(bits, ranks[0] + t * tb, i);", "double s = decode_value(bits, ranks[0] + t * tb, i);"),
+        ("float s = decode_value_fmt(fmt_in, ranks[0] + t * tb, i);",
+         "double s = decode_value_fmt(fmt_in, ranks[0] + t * tb, i);"),
         ("z[i] = dtype_to_f32(dtype, f32_to_dtype(dtype, s));",
          "z[i] = dtype_to_f32(dtype, f32_to_dtype(dtype, (float)s));")]),
     ("sum not rounded to dtype", [("z[i] = dtype_to_f32(dtype, f32_to_dtype(dtype, s));", "z[i] = s;")]),
-    ("terms rounded to dtype", [("s = s + decode_value(bits, ranks[r] + t * tb, i);",
-                                 "s = s + dtype_to_f32(dtype, f32_to_dtype(dtype, decode_value(bits, ranks[r] + t * tb, i)));")]),
+    ("terms rounded to dtype", [("s = s + decode_value_fmt(fmt_in, ranks[r] + t * tb, i);",
+                                 "s = s + dtype_to_f32(dtype, f32_to_dtype(dtype, decode_value_fmt(fmt_in, ranks[r] + t * tb, i)));")]),
     ("fp16 ties away from zero", [("  float r = rintf(a / quantum) * quantum;\n  if (r < 0x1p-14f)",
                                    "  float r = roundf(a / quantum) * quantum;\n  if (r < 0x1p-14f)")]),
     ("bf16 truncation", [("float r = rintf(a / quantum) * quantum; /* exact scaling, ties to even */",
@@ -83,12 +84,29 @@ MUTANTS = [
     ("fp16 subnormal decode scale", [("mag = ldexpf((float)frac, -24);", "mag = ldexpf((float)frac, -25);")]),
     ("block of 16 values", [("#define QRO_BLOCK 32 ", "#define QRO_BLOCK 16 ")]),
     ("output decoded before re-encode", [
-        ("y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value(obits, out, i));",
+        ("y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value_fmt(fmt_out, out, i));",
          "y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, z[i]);")]),
-    ("mixed: re-encode in the input format", [("encode_tile(obits, z, out);", "encode_tile(bits, z, out);")]),
+    ("mixed: re-encode in the input format", [("encode_tile_fmt(fmt_out, z, out);", "encode_tile_fmt(fmt_in, z, out);")]),
     ("mixed: final decode in the input format", [
-        ("y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value(obits, out, i));",
-         "y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value(bits, out, i));")]),
+        ("y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value_fmt(fmt_out, out, i));",
+         "y_out[t * QRO_TILE + i] = f32_to_dtype(dtype, decode_value_fmt(fmt_in, out, i));")]),
+    ("asym: range excludes zero", [("float lo = 0.0f, hi = 0.0f; /* the range always includes 0 */",
+                                    "float lo = x[0], hi = x[0];")]),
+    ("asym: divides the range by 2^b", [("float t = (hi - lo) / (float)qmax;", "float t = (hi - lo) / (float)(qmax + 1);")]),
+    ("asym: zero point not added", [("long k = lrintf(u) + *z;", "long k = lrintf(u);")]),
+    ("asym: decode ignores the zero point", [("return (float)((int)get_code(bits, tile, i) - z) * d;",
+                                              "return (float)((int)get_code(bits, tile, i)) * d;")]),
+    ("asym: zero point not clamped", [("zf = fminf(fmaxf(zf, 0.0f), (float)qmax);", "")]),
+    ("asym: codes clamp at qmax - 1", [("if (k > qmax) k = qmax;", "if (k > qmax - 1) k = qmax - 1;")]),
+    ("asym: zero points overlap the codes", [("asym_scale_offset(bits) + 2 * QRO_AGROUPS; }",
+                                              "asym_scale_offset(bits) - QRO_AGROUPS; }")]),
+    ("asym: group scale not saturated", [("if (t > 65504.0f) t = 65504.0f; /* saturate the group scale */", "")]),
+    ("asym: multiplier rounded to fp16", [("*e = (d == 0.0f) ? 0.0f : 1.0f / d; /* group multiplier */",
+                                           "*e = (d == 0.0f) ? 0.0f : qro_f16_to_f32(qro_f32_to_f16(1.0f / d));")]),
+    ("asym: divide by the scale", [("float u = x[i] * e;",
+                                    "float u = (e == 0.0f) ? 0.0f : x[i] / qro_f16_to_f32(*d_bits);")]),
+    ("asym: zero point truncated", [("float zf = rintf(-lo * *e);", "float zf = truncf(-lo * *e);")]),
+    ("asym: groups of 64", [("#define QRO_AGROUP 128 ", "#define QRO_AGROUP 64 ")]),
 ]
 
 
