@@ -334,9 +334,11 @@ static void encode_group_asym(int bits, const float x[QRO_AGROUP], unsigned code
   qro_group_params(bits, lo, hi, d_bits, &e, z);
   for (int i = 0; i < QRO_AGROUP; ++i) {
     float u = x[i] * e;
-    long k = lrintf(u) + *z;
-    if (k < 0) k = 0;
-    if (k > qmax) k = qmax;
+    /* rint(u) + z in binary32: exact while |u| < 2^24, and an infinite u (a
+       sum that overflowed the I/O dtype) stays infinite, so the clamp sends
+       it to the end of the range, as the definition does */
+    float k = rintf(u) + (float)*z;
+    k = fminf(fmaxf(k, 0.0f), (float)qmax);
     codes[i] = (unsigned)k;
   }
 }

@@ -951,6 +951,34 @@ def pin_asym_reduce_exact(o, seed=23):
                               <= np.repeat(d8, AGROUP) * 0.51 + np.abs((tot * s[:, None]).ravel()) * 2.0 ** -7)
 
 
+def pin_asym_overflow_sum(o):
+    """fp16 sums beyond the largest finite value round to +-inf (IEEE
+    overflow).  In a group with +inf, hi = inf, so the scale saturates at 65504
+    (0x7BFF); lo = 0 gives z = 0, and the code of +inf is rint(inf) + 0
+    clamped to qmax; decode gives qmax * 65504, which is inf again in fp16.
+    With -inf as well, -lo * e = inf clamps z to qmax and -inf codes to 0
+    (decoding to -qmax * 65504 = -inf), while +inf codes to qmax = z and so
+    decodes to 0."""
+    for bits, fid in ASYM.items():
+        qmax = (1 << bits) - 1
+        a = np.zeros(TILE)
+        a[:AGROUP] = 1.0
+        a[0:3] = 60000.0                              # + 60000 below -> 120000 -> +inf
+        a[AGROUP:AGROUP + 2] = [60000.0, -60000.0]    # group 1: +inf and -inf
+        b = np.zeros(TILE)
+        b[0:3] = 60000.0
+        b[AGROUP:AGROUP + 2] = [60000.0, -60000.0]
+        ra = o.encode(fid, "fp16", f16_bits(a))
+        rb = o.encode(fid, "fp16", f16_bits(b))
+        out, y = o.reduce(fid, "fp16", [ra, rb], TILE)
+        codes, sb, zp = asym_unpack(bits, out)
+        assert sb[0, 0] == 0x7BFF and zp[0, 0] == 0, (bits, hex(sb[0, 0]), zp[0, 0])
+        assert np.all(codes[0, 0:3] == qmax), (bits, codes[0, :3])
+        assert sb[0, 1] == 0x7BFF and zp[0, 1] == qmax, (bits, zp[0, 1])
+        assert codes[0, AGROUP] == qmax and codes[0, AGROUP + 1] == 0, (bits, codes[0, AGROUP:AGROUP + 2])
+        assert np.all(y[0:3] == 0x7C00) and y[AGROUP] == 0 and y[AGROUP + 1] == 0xFC00, bits
+
+
 def pin_asym_error_bound(o, seed=24):
     """|decode(encode(x)) - x| <= (0.5 + qmax * 2^-11) * s for every value: inside
     the grid the error is half a step; the fp16 rounding of the scale can leave
@@ -1073,6 +1101,7 @@ ALL_PINS = [
     pin_asym_decode_algorithm1,
     pin_asym_reduce_exact,
     pin_asym_zero_point_clamp,
+    pin_asym_overflow_sum,
     pin_asym_error_bound,
     pin_error_bound,
 ]

@@ -93,11 +93,11 @@ MUTANTS = [
     ("asym: range excludes zero", [("float lo = 0.0f, hi = 0.0f; /* the range always includes 0 */",
                                     "float lo = x[0], hi = x[0];")]),
     ("asym: divides the range by 2^b", [("float t = (hi - lo) / (float)qmax;", "float t = (hi - lo) / (float)(qmax + 1);")]),
-    ("asym: zero point not added", [("long k = lrintf(u) + *z;", "long k = lrintf(u);")]),
+    ("asym: zero point not added", [("float k = rintf(u) + (float)*z;", "float k = rintf(u);")]),
     ("asym: decode ignores the zero point", [("return (float)((int)get_code(bits, tile, i) - z) * d;",
                                               "return (float)((int)get_code(bits, tile, i)) * d;")]),
     ("asym: zero point not clamped", [("zf = fminf(fmaxf(zf, 0.0f), (float)qmax);", "")]),
-    ("asym: codes clamp at qmax - 1", [("if (k > qmax) k = qmax;", "if (k > qmax - 1) k = qmax - 1;")]),
+    ("asym: codes clamp at qmax - 1", [("k = fminf(fmaxf(k, 0.0f), (float)qmax);", "k = fminf(fmaxf(k, 0.0f), (float)(qmax - 1));")]),
     ("asym: zero points overlap the codes", [("asym_scale_offset(bits) + 2 * QRO_AGROUPS; }",
                                               "asym_scale_offset(bits) - QRO_AGROUPS; }")]),
     ("asym: group scale not saturated", [("if (t > 65504.0f) t = 65504.0f; /* saturate the group scale */", "")]),
@@ -106,6 +106,8 @@ MUTANTS = [
     ("asym: divide by the scale", [("float u = x[i] * e;",
                                     "float u = (e == 0.0f) ? 0.0f : x[i] / qro_f16_to_f32(*d_bits);")]),
     ("asym: zero point truncated", [("float zf = rintf(-lo * *e);", "float zf = truncf(-lo * *e);")]),
+    ("asym: no clamp at the top", [("k = fminf(fmaxf(k, 0.0f), (float)qmax);", "k = fmaxf(k, 0.0f);")]),
+    ("asym: rounding after the zero point", [("float k = rintf(u) + (float)*z;", "float k = rintf(u + (float)*z);")]),
     ("asym: groups of 64", [("#define QRO_AGROUP 128 ", "#define QRO_AGROUP 64 ")]),
 ]
 
