@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GB/s of FP16 input through encode+compressed-reduce+decode; % HBM peak"
 PEAK_HBM_GBS = 8000.0
-TILE_BYTES = {"int3": 896, "int4": 1152, "int8": 2176}
+TILE_BYTES = {"int3": 896, "int4": 1152, "int8": 2176, "asym4": 1072, "asym8": 2096}
+FORMAT_IDS = {"int3": 3, "int4": 4, "int8": 8, "asym4": 20, "asym8": 24}
 KERNEL_SOURCES = ["bit_quantized_all_amd/csrc/qr_kernels.hpp", "bit_quantized_all_amd/csrc/qr_codec.hpp"]
 
 
@@ -121,8 +122,8 @@ def cpu_baseline(w, xs, out, y, seconds):
     import oracle
 
     o = oracle.default()
-    bits = {"int3": 3, "int4": 4, "int8": 8}[w.fmt]
-    obits = {"int3": 3, "int4": 4, "int8": 8}[w.out_fmt]
+    bits = FORMAT_IDS[w.fmt]
+    obits = FORMAT_IDS[w.out_fmt]
     tb = TILE_BYTES[w.out_fmt]
     ntiles = w.n // 2048
     chunk = 16

@@ -12,9 +12,11 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 _CSRC = os.path.join(HERE, "csrc")
-# (source, extra flags): the mixed-format reduce is built once per input format
+# (source, extra flags): the mixed-format and asymmetric reduces are built once
+# per input format
 SOURCES = [(os.path.join(_CSRC, "qr_api.hip"), [])] + [
-    (os.path.join(_CSRC, "qr_reduce_mixed.hip"), [f"-DQR_MIXED_IN={b}"]) for b in (3, 4, 8)]
+    (os.path.join(_CSRC, "qr_reduce_mixed.hip"), [f"-DQR_MIXED_IN={b}"]) for b in (3, 4, 8)] + [
+    (os.path.join(_CSRC, "qr_asym.hip"), [f"-DQR_ASYM_IN={f}"]) for f in (20, 24)]
 LIB = os.path.join(HERE, "libqr.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -9,6 +9,14 @@
 //   INT3   2-bit plane (uint16 per unit, value j at bits 2j) + 1-bit plane
 //          (uint8 per unit, value j at bit j)
 //   decode = (code - Q) * d, exact in fp32.
+// Asymmetric group codec (the "Flash Communication" review of arXiv
+// 2412.04964, fields pith_summary / key_machinery: group size 128, a scale and
+// a zero point per group; minor_comments on Algorithm 1: (q - z) * s):
+//   group  = 128 consecutive values, range [lo, hi] = [min(x, 0), max(x, 0)]
+//   scale  s = fp16(min((hi - lo) / (2^b - 1), 65504)), e = fp32(1/s) (0 if s == 0)
+//   zero   z = clamp(rint(-lo * e), 0, 2^b - 1), one byte per group
+//   code   q = clamp(rint(x * e) + z, 0, 2^b - 1), packed as the INT4 / INT8 codes
+//   decode = (q - z) * s, exact in fp32.
 //
 // Work mapping: one lane owns one block (32 values), one 64-lane wave owns one
 // 2048-value tile.  The block maximum and the scale are computed once per
@@ -36,10 +44,14 @@ constexpr int kChunks = kTileValues * 2 / 16;  // 16-byte chunks of one fp16/bf1
 
 enum { kFp16 = 0, kBf16 = 1 };
 
-template <int BITS>
+// Formats are named by their qr_format value: 3, 4, 8 (symmetric, 32-value
+// blocks) and 20, 24 (asymmetric, 128-value groups, 4- and 8-bit codes).
+template <int F>
 struct Format;
 template <>
 struct Format<3> {
+  static constexpr bool kAsym = false;
+  static constexpr int kCodeBits = 3;
   static constexpr int kQ = 4;
   static constexpr int kTileBytes = 896;   // 512 (2-bit plane) + 256 (1-bit plane) + 128
   static constexpr int kScaleOffset = 768;
@@ -48,6 +60,8 @@ struct Format<3> {
 };
 template <>
 struct Format<4> {
+  static constexpr bool kAsym = false;
+  static constexpr int kCodeBits = 4;
   static constexpr int kQ = 8;
   static constexpr int kTileBytes = 1152;  // 1024 + 128
   static constexpr int kScaleOffset = 1024;
@@ -55,28 +69,52 @@ struct Format<4> {
 };
 template <>
 struct Format<8> {
+  static constexpr bool kAsym = false;
+  static constexpr int kCodeBits = 8;
   static constexpr int kQ = 128;
   static constexpr int kTileBytes = 2176;  // 2048 + 128
   static constexpr int kScaleOffset = 2048;
   static constexpr int kShift = 0;
 };
-
-// Packed codes of one block as held by its lane.
-template <int BITS>
-struct Block;
 template <>
-struct Block<4> {
+struct Format<20> {
+  static constexpr bool kAsym = true;
+  static constexpr int kCodeBits = 4;
+  static constexpr int kQmax = 15;
+  static constexpr int kTileBytes = 1072;  // 1024 codes + 16 fp16 scales + 16 zero points
+  static constexpr int kScaleOffset = 1024;
+  static constexpr int kZeroOffset = 1056;
+  static constexpr int kShift = 0;
+};
+template <>
+struct Format<24> {
+  static constexpr bool kAsym = true;
+  static constexpr int kCodeBits = 8;
+  static constexpr int kQmax = 255;
+  static constexpr int kTileBytes = 2096;  // 2048 codes + 16 fp16 scales + 16 zero points
+  static constexpr int kScaleOffset = 2048;
+  static constexpr int kZeroOffset = 2080;
+  static constexpr int kShift = 0;
+};
+
+// Packed codes of one 32-value block as held by its lane, by code width.
+template <int CB>
+struct CodeBlock;
+template <>
+struct CodeBlock<4> {
   uint32_t w[4];  // units 0..3
 };
 template <>
-struct Block<3> {
+struct CodeBlock<3> {
   uint32_t low[2];  // 2-bit plane: units 0,1 in low[0] (unit 0 in bits 0..15), units 2,3 in low[1]
   uint32_t high;    // 1-bit plane: byte u = unit u
 };
 template <>
-struct Block<8> {
+struct CodeBlock<8> {
   uint32_t w[8];  // byte i of the block = value i
 };
+template <int F>
+using Block = CodeBlock<Format<F>::kCodeBits>;
 
 // ---------------------------------------------------------------------------
 // dtype <-> fp32
@@ -253,8 +291,9 @@ __device__ __forceinline__ float code_value(uint32_t t) {
 }
 
 // Packs 32 codes (low byte of each t[i]) into the lane's block.
-template <int BITS>
-__device__ __forceinline__ void pack_block(const uint32_t (&t)[kBlockValues], Block<BITS>& blk) {
+template <int F>
+__device__ __forceinline__ void pack_block(const uint32_t (&t)[kBlockValues], Block<F>& blk) {
+  constexpr int BITS = Format<F>::kCodeBits;
   if constexpr (BITS == 4) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) blk.w[u] = pack_int4_unit(t + 8 * u);
@@ -318,8 +357,10 @@ __device__ __forceinline__ uint32_t quantize_words(const uint32_t (&w)[kBlockVal
 
 // Decodes one block into kk[i] = 2^Format::kShift * (code_i - Q) as fp32.
 // The value is kk[i] * (d * 2^-kShift), an exact product.
-template <int BITS>
-__device__ __forceinline__ void decode_block(const Block<BITS>& blk, float (&kk)[kBlockValues]) {
+template <int F>
+__device__ __forceinline__ void decode_block(const Block<F>& blk, float (&kk)[kBlockValues]) {
+  constexpr int BITS = Format<F>::kCodeBits;
+  static_assert(!Format<F>::kAsym, "asymmetric formats decode with decode_block_asym");
   if constexpr (BITS == 4) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -361,6 +402,135 @@ __device__ __forceinline__ void decode_block(const Block<BITS>& blk, float (&kk)
 }
 
 // ---------------------------------------------------------------------------
+// asymmetric group codec: a group of 128 values is the blocks of four
+// consecutive lanes (lanes 4g..4g+3 of a wave hold group g of its tile)
+// ---------------------------------------------------------------------------
+
+// Maximum over the four lanes of a group (DPP quad permutes [1,0,3,2] and
+// [2,3,0,1]; every lane of the wave is active).
+template <int CTRL>
+__device__ __forceinline__ int quad_perm(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int group_max_i32(int v) {
+  v = __builtin_elementwise_max(v, quad_perm<0xB1>(v));
+  return __builtin_elementwise_max(v, quad_perm<0x4E>(v));
+}
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  v = __builtin_elementwise_max(v, (uint32_t)quad_perm<0xB1>((int)v));
+  return __builtin_elementwise_max(v, (uint32_t)quad_perm<0x4E>((int)v));
+}
+
+// fp32 value of an fp16 / bf16 bit pattern held in the low 16 bits.
+template <int DT>
+__device__ __forceinline__ float half_pattern_to_f32(uint32_t h) {
+  if constexpr (DT == kFp16)
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  else
+    return __builtin_bit_cast(float, h << 16);
+}
+
+// Scale, multiplier and zero point of a group with range [lo, hi], lo <= 0 <= hi:
+// s = fp16(min(RN32(RN32(hi - lo) / qmax), 65504)) (a correctly rounded fp32
+// division), e = fp32(1 / s) (0 if s == 0), z = clamp(rint(RN32(-lo * e)), 0, qmax).
+// Returns s's bits | z << 16.
+template <int F>
+__device__ __forceinline__ uint32_t group_params(float lo, float hi, float& d, float& e, float& z) {
+  constexpr float kQmax = (float)Format<F>::kQmax;
+  const float t = (hi - lo) / kQmax;
+  const _Float16 dh = (_Float16)__builtin_fminf(t, 65504.0f);
+  d = (float)dh;
+  e = (d == 0.0f) ? 0.0f : recip_fp16_value(d);
+  z = __builtin_amdgcn_fmed3f(__builtin_rintf(-lo * e), 0.0f, kQmax);
+  return (uint32_t)__builtin_bit_cast(uint16_t, dh) | ((uint32_t)z << 16);
+}
+
+// Code of one value, q = clamp(rint(v) + z, 0, qmax), as the bits of 2^23 + q
+// (low byte = q); zb = z - 256.  Adding 2^23 + 256 (even) rounds v to an
+// integer with ties to even for every v >= -256; adding z first would move
+// ties for odd z.  Smaller v, and large v, land outside [2^23, 2^23 + qmax]
+// and clamp to the ends, as the clamp of rint(v) + z does.
+template <int F>
+__device__ __forceinline__ uint32_t quantize_asym(float v, float zb) {
+  const float r = v + 8388864.0f;  // 2^23 + 256
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(r + zb, 8388608.0f,
+                                                              8388608.0f + Format<F>::kQmax));
+}
+
+// (q - z) as fp32 from quantize_asym()'s result; zm = 2^23 + z (exact).
+__device__ __forceinline__ float code_value_asym(uint32_t t, float zm) {
+  return __builtin_bit_cast(float, t) - zm;
+}
+
+// Quantizes one lane's block of a group given as 16 packed fp16/bf16 words;
+// the four lanes of the group share the range.  Returns scale bits | z << 16.
+// The range ends come from two integer maxima of the sign-magnitude bit
+// patterns, with no float compares: hi = max(x, 0) is the signed maximum of
+// the patterns and 0 (every negative pattern is a negative integer), and the
+// unsigned maximum is the negative value of largest magnitude when there is
+// one (sign bit set), else non-negative (then min(x, 0) = 0).  Inputs are finite.
+template <int F, int DT>
+__device__ __forceinline__ uint32_t quantize_words_asym(const uint32_t (&w)[kBlockValues / 2],
+                                                        uint32_t (&t)[kBlockValues]) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  s16x2 smax = {0, 0};
+  u16x2 umax = {0, 0};
+#pragma unroll
+  for (int j = 0; j < kBlockValues / 2; ++j) {
+    smax = __builtin_elementwise_max(smax, __builtin_bit_cast(s16x2, w[j]));
+    umax = __builtin_elementwise_max(umax, __builtin_bit_cast(u16x2, w[j]));
+  }
+  const int hb = group_max_i32(smax.x > smax.y ? smax.x : smax.y);
+  const uint32_t lb = group_max_u32(umax.x > umax.y ? umax.x : umax.y);
+  const float hi = half_pattern_to_f32<DT>((uint32_t)hb);
+  const float lo = (lb & 0x8000u) ? half_pattern_to_f32<DT>(lb) : 0.0f;
+  float d, e, z;
+  const uint32_t params = group_params<F>(lo, hi, d, e, z);
+  const float zb = z - 256.0f;
+#pragma unroll
+  for (int j = 0; j < kBlockValues / 2; ++j) {
+    float v0, v1;
+    scale_pair<DT>(w[j], e, v0, v1);
+    t[2 * j] = quantize_asym<F>(v0, zb);
+    t[2 * j + 1] = quantize_asym<F>(v1, zb);
+  }
+  return params;
+}
+
+// Decodes one block of an asymmetric format into kk[i] = q_i - z (exact).
+//   4-bit: per byte (q + 128 - z) ^ 0x80 = q - z as int8 (q + 128 - z lies in
+//          [113, 143], so the byte-wise add never carries)
+//   8-bit: per 16-bit half q - z as int16 (packed subtract)
+template <int F>
+__device__ __forceinline__ void decode_block_asym(const Block<F>& blk, uint32_t z, float (&kk)[kBlockValues]) {
+  if constexpr (Format<F>::kCodeBits == 4) {
+    const uint32_t c = (0x80u - z) * 0x01010101u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t ev = ((blk.w[u] & 0x0F0F0F0Fu) + c) ^ 0x80808080u;         // values 8u + 2i
+      const uint32_t od = (((blk.w[u] >> 4) & 0x0F0F0F0Fu) + c) ^ 0x80808080u;  // values 8u + 2i + 1
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kk[8 * u + 2 * i] = sbyte(ev, i);
+        kk[8 * u + 2 * i + 1] = sbyte(od, i);
+      }
+    }
+  } else {
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    const s16x2 zz = {(short)z, (short)z};
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const s16x2 ev = __builtin_bit_cast(s16x2, blk.w[w] & 0x00FF00FFu) - zz;         // values 4w, 4w + 2
+      const s16x2 od = __builtin_bit_cast(s16x2, (blk.w[w] >> 8) & 0x00FF00FFu) - zz;  // values 4w + 1, 4w + 3
+      kk[4 * w + 0] = (float)ev.x;
+      kk[4 * w + 1] = (float)od.x;
+      kk[4 * w + 2] = (float)ev.y;
+      kk[4 * w + 3] = (float)od.y;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // global <-> lane block data
 // ---------------------------------------------------------------------------
 
@@ -382,9 +552,12 @@ __device__ __forceinline__ void st(T v, T* p) {
     *p = v;
 }
 
-template <int BITS, bool NT>
-__device__ __forceinline__ void load_block(const uint8_t* __restrict__ tile, int g, Block<BITS>& blk,
+// Codes of block g and its scale; for the asymmetric formats the scale and
+// zero point of the block's group (scale bits | zero point << 16).
+template <int F, bool NT>
+__device__ __forceinline__ void load_block(const uint8_t* __restrict__ tile, int g, Block<F>& blk,
                                            uint32_t& scale) {
+  constexpr int BITS = Format<F>::kCodeBits;
   if constexpr (BITS == 4) {
     const u32x4 v = ld<NT>(reinterpret_cast<const u32x4*>(tile + 16 * g));
     blk.w[0] = v.x; blk.w[1] = v.y; blk.w[2] = v.z; blk.w[3] = v.w;
@@ -398,12 +571,21 @@ __device__ __forceinline__ void load_block(const uint8_t* __restrict__ tile, int
     blk.low[0] = lw.x; blk.low[1] = lw.y;
     blk.high = ld<NT>(reinterpret_cast<const uint32_t*>(tile + Format<3>::kHighOffset + 4 * g));
   }
-  scale = ld<NT>(reinterpret_cast<const uint16_t*>(tile + Format<BITS>::kScaleOffset + 2 * g));
+  if constexpr (Format<F>::kAsym) {
+    const int grp = g >> 2;
+    scale = ld<NT>(reinterpret_cast<const uint16_t*>(tile + Format<F>::kScaleOffset + 2 * grp)) |
+            ((uint32_t)ld<NT>(tile + Format<F>::kZeroOffset + grp) << 16);
+  } else {
+    scale = ld<NT>(reinterpret_cast<const uint16_t*>(tile + Format<F>::kScaleOffset + 2 * g));
+  }
 }
 
-template <int BITS, bool NT>
-__device__ __forceinline__ void store_block(uint8_t* __restrict__ tile, int g, const Block<BITS>& blk,
+// Stores block g; for the asymmetric formats the first lane of each group
+// stores the group's scale and zero point (scale bits | zero point << 16).
+template <int F, bool NT>
+__device__ __forceinline__ void store_block(uint8_t* __restrict__ tile, int g, const Block<F>& blk,
                                             uint32_t scale) {
+  constexpr int BITS = Format<F>::kCodeBits;
   if constexpr (BITS == 4) {
     st<NT>(u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]}, reinterpret_cast<u32x4*>(tile + 16 * g));
   } else if constexpr (BITS == 8) {
@@ -413,7 +595,15 @@ __device__ __forceinline__ void store_block(uint8_t* __restrict__ tile, int g, c
     st<NT>(u32x2{blk.low[0], blk.low[1]}, reinterpret_cast<u32x2*>(tile + 8 * g));
     st<NT>(blk.high, reinterpret_cast<uint32_t*>(tile + Format<3>::kHighOffset + 4 * g));
   }
-  st<NT>((uint16_t)scale, reinterpret_cast<uint16_t*>(tile + Format<BITS>::kScaleOffset + 2 * g));
+  if constexpr (Format<F>::kAsym) {
+    if ((g & 3) == 0) {
+      const int grp = g >> 2;
+      st<NT>((uint16_t)scale, reinterpret_cast<uint16_t*>(tile + Format<F>::kScaleOffset + 2 * grp));
+      st<NT>((uint8_t)(scale >> 16), tile + Format<F>::kZeroOffset + grp);
+    }
+  } else {
+    st<NT>((uint16_t)scale, reinterpret_cast<uint16_t*>(tile + Format<F>::kScaleOffset + 2 * g));
+  }
 }
 
 // fp32 of an fp16 scale held in the low 16 bits.

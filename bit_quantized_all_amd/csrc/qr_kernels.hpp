@@ -55,11 +55,6 @@ namespace qr {
 #ifndef QR_ENC_TILES_PER_WAVE
 #define QR_ENC_TILES_PER_WAVE 1
 #endif
-// Encode mapping: 0 = lane per 32-value block through an LDS transpose,
-// 1 = lane per 8-value unit with a 4-lane DPP block maximum.
-#ifndef QR_ENC_QUAD
-#define QR_ENC_QUAD 0
-#endif
 // 1: issue every rank's loads before decoding; 0: let the scheduler pipeline them.
 #ifndef QR_RED_LOADS_FIRST
 #define QR_RED_LOADS_FIRST 1
@@ -103,78 +98,14 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restr
     }
     wave_lds_sync();  // the next tile overwrites this LDS tile
     uint32_t t[kBlockValues];
-    const uint32_t scale = quantize_words<BITS, DT>(w, t);
+    uint32_t scale;
+    if constexpr (Format<BITS>::kAsym)
+      scale = quantize_words_asym<BITS, DT>(w, t);
+    else
+      scale = quantize_words<BITS, DT>(w, t);
     Block<BITS> blk;
     pack_block<BITS>(t, blk);
     store_block<BITS, QR_ENC_NT_STORE>(packed + (size_t)tile * Format<BITS>::kTileBytes, lane, blk, scale);
-  }
-}
-
-// Alternative encode mapping: lane = one 8-value unit (a coalesced 16-byte
-// load straight into registers), four lanes per block; the block maximum is
-// reduced across the 4-lane group with DPP quad permutes and every lane of
-// the group derives the same scale.  No LDS.
-__device__ __forceinline__ float quad_max(float m) {
-  // quad_perm [1,0,3,2] then [2,3,0,1]
-  m = __builtin_fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0xB1, 0xF, 0xF, false)));
-  m = __builtin_fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0x4E, 0xF, 0xF, false)));
-  return m;
-}
-
-template <int BITS, int DT>
-__global__ __launch_bounds__(kThreads) void encode_quad_kernel(const uint8_t* __restrict__ x,
-                                                               uint8_t* __restrict__ packed, int ntiles) {
-  constexpr int TB = Format<BITS>::kTileBytes;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  for (int tile = blockIdx.x * kWavesPerGroup + wave; tile < ntiles; tile += gridDim.x * kWavesPerGroup) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)tile * (kTileValues * 2));
-    uint8_t* dst = packed + (size_t)tile * TB;
-    u32x4 v[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = ld<QR_ENC_NT_LOAD>(src + lane + kWave * k);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int u = kWave * k + lane;  // unit index in the tile
-      const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-      float z[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        z[2 * q] = lo_to_f32<DT>(w[q]);
-        z[2 * q + 1] = hi_to_f32<DT>(w[q]);
-      }
-      float m = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(z[i]));
-      m = quad_max(m);
-      float d, e;
-      const uint32_t scale = block_scale<BITS>(m, d, e);
-      uint32_t t[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) t[i] = quantize<BITS>(z[i] * e);
-      if constexpr (BITS == 4) {
-        st<QR_ENC_NT_STORE>(pack_int4_unit(t), reinterpret_cast<uint32_t*>(dst + 4 * u));
-      } else if constexpr (BITS == 8) {
-        st<QR_ENC_NT_STORE>(u32x2{pack_int8_word(t), pack_int8_word(t + 4)}, reinterpret_cast<u32x2*>(dst + 8 * u));
-      } else {
-        // bytes c0 c2 c4 c6 and c1 c3 c5 c7 -> 2-bit plane word and 1-bit plane byte
-        const uint32_t ev = lo_pair(t[0], t[2]) | hi_pair(t[4], t[6]);
-        const uint32_t od = lo_pair(t[1], t[3]) | hi_pair(t[5], t[7]);
-        const uint32_t nib = ev | (od << 4);           // nibble j = code j (INT4 order)
-        uint32_t lo = nib & 0x33333333u;               // low pairs at bits 4j
-        lo = (lo | (lo >> 2)) & 0x0F0F0F0Fu;
-        lo = (lo | (lo >> 4)) & 0x00FF00FFu;
-        lo = (lo | (lo >> 8)) & 0x0000FFFFu;
-        uint32_t hb = (nib >> 2) & 0x11111111u;        // high bits at bits 4j
-        hb = (hb | (hb >> 3)) & 0x03030303u;
-        hb = (hb | (hb >> 6)) & 0x000F000Fu;
-        hb = (hb | (hb >> 12)) & 0x000000FFu;
-        st<QR_ENC_NT_STORE>((uint16_t)lo, reinterpret_cast<uint16_t*>(dst + 2 * u));
-        st<QR_ENC_NT_STORE>((uint8_t)hb, dst + Format<3>::kHighOffset + u);
-      }
-      if ((lane & 3) == 0)
-        st<QR_ENC_NT_STORE>((uint16_t)scale, reinterpret_cast<uint16_t*>(dst + Format<BITS>::kScaleOffset + 2 * (u >> 2)));
-    }
   }
 }
 
@@ -217,8 +148,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint8_t* __restr
     uint32_t scale;
     load_block<BITS, QR_DEC_NT_LOAD>(packed + (size_t)tile * Format<BITS>::kTileBytes, lane, blk, scale);
     float kk[kBlockValues];
-    decode_block<BITS>(blk, kk);
-    const float dd = scale_f32(scale) * (1.0f / (1 << Format<BITS>::kShift));
+    float dd;
+    if constexpr (Format<BITS>::kAsym) {
+      decode_block_asym<BITS>(blk, scale >> 16, kk);
+      dd = scale_f32(scale);
+    } else {
+      decode_block<BITS>(blk, kk);
+      dd = scale_f32(scale) * (1.0f / (1 << Format<BITS>::kShift));
+    }
     float v[kBlockValues];
 #pragma unroll
     for (int i = 0; i < kBlockValues; ++i) v[i] = kk[i] * dd;
@@ -261,8 +198,14 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float kk[kBlockValues];
-      decode_block<BI>(blk[r], kk);
-      const float dd = scale_f32(sc[r]) * kInvShift;
+      float dd;
+      if constexpr (Format<BI>::kAsym) {
+        decode_block_asym<BI>(blk[r], sc[r] >> 16, kk);
+        dd = scale_f32(sc[r]);
+      } else {
+        decode_block<BI>(blk[r], kk);
+        dd = scale_f32(sc[r]) * kInvShift;
+      }
       if (r == 0) {
 #pragma unroll
         for (int i = 0; i < kBlockValues; ++i) s[i] = kk[i] * dd;
@@ -272,25 +215,59 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
       }
     }
     // re-encode dtype_RNE(s): rounding is monotonic and symmetric, so the
-    // block maximum of the rounded values is the rounded maximum of |s|
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kBlockValues; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(s[i]));
-    float d, e;
-    const uint32_t scale = block_scale<BO>(round_to_dtype<DT>(m), d, e);
+    // block maximum (group range) of the rounded values is the rounded
+    // maximum of |s| (range of s)
     uint32_t t[kBlockValues];
+    uint32_t scale;
+    if constexpr (Format<BO>::kAsym) {
+      // range ends from integer maxima of the fp32 patterns (as in quantize_words_asym)
+      int hb = 0;
+      uint32_t lb = 0;
 #pragma unroll
-    for (int i = 0; i < kBlockValues; i += 2) {
-      float v0, v1;
-      round_scale2<DT>(s[i], s[i + 1], e, v0, v1);
-      t[i] = quantize<BO>(v0);
-      t[i + 1] = quantize<BO>(v1);
-    }
-    if constexpr (WITH_Y) {  // decode of the re-encoded sum, straight from the codes
-      float v[kBlockValues];
+      for (int i = 0; i < kBlockValues; ++i) {
+        hb = __builtin_elementwise_max(hb, __builtin_bit_cast(int, s[i]));
+        lb = __builtin_elementwise_max(lb, __builtin_bit_cast(uint32_t, s[i]));
+      }
+      hb = group_max_i32(hb);
+      lb = group_max_u32(lb);
+      const float hi = round_to_dtype<DT>(__builtin_bit_cast(float, hb));
+      const float lo = (lb & 0x80000000u) ? round_to_dtype<DT>(__builtin_bit_cast(float, lb)) : 0.0f;
+      float d, e, z;
+      scale = group_params<BO>(lo, hi, d, e, z);
+      const float zb = z - 256.0f;
 #pragma unroll
-      for (int i = 0; i < kBlockValues; ++i) v[i] = code_value<BO>(t[i]) * d;
-      write_lane_values<DT>(lds[wave], lane, v);
+      for (int i = 0; i < kBlockValues; i += 2) {
+        float v0, v1;
+        round_scale2<DT>(s[i], s[i + 1], e, v0, v1);
+        t[i] = quantize_asym<BO>(v0, zb);
+        t[i + 1] = quantize_asym<BO>(v1, zb);
+      }
+      if constexpr (WITH_Y) {  // decode of the re-encoded sum, straight from the codes
+        const float zm = 8388608.0f + z;
+        float v[kBlockValues];
+#pragma unroll
+        for (int i = 0; i < kBlockValues; ++i) v[i] = code_value_asym(t[i], zm) * d;
+        write_lane_values<DT>(lds[wave], lane, v);
+      }
+    } else {
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kBlockValues; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(s[i]));
+      float d, e;
+      scale = block_scale<BO>(round_to_dtype<DT>(m), d, e);
+#pragma unroll
+      for (int i = 0; i < kBlockValues; i += 2) {
+        float v0, v1;
+        round_scale2<DT>(s[i], s[i + 1], e, v0, v1);
+        t[i] = quantize<BO>(v0);
+        t[i + 1] = quantize<BO>(v1);
+      }
+      if constexpr (WITH_Y) {  // decode of the re-encoded sum, straight from the codes
+        float v[kBlockValues];
+#pragma unroll
+        for (int i = 0; i < kBlockValues; ++i) v[i] = code_value<BO>(t[i]) * d;
+        write_lane_values<DT>(lds[wave], lane, v);
+      }
     }
     Block<BO> ob;
     pack_block<BO>(t, ob);
@@ -313,18 +290,12 @@ inline dim3 grid_for(size_t ntiles) {
 template <int BITS>
 qr_status launch_encode(int dt, const void* x, void* p, size_t ntiles, hipStream_t st) {
   const dim3 grid = grid_for((ntiles + QR_ENC_TILES_PER_WAVE - 1) / QR_ENC_TILES_PER_WAVE);
-#if QR_ENC_QUAD
-#define QR_ENCODE_KERNEL encode_quad_kernel
-#else
-#define QR_ENCODE_KERNEL encode_kernel
-#endif
   if (dt == kFp16)
-    hipLaunchKernelGGL((QR_ENCODE_KERNEL<BITS, kFp16>), grid, dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((encode_kernel<BITS, kFp16>), grid, dim3(kThreads), 0, st,
                        (const uint8_t*)x, (uint8_t*)p, (int)ntiles);
   else
-    hipLaunchKernelGGL((QR_ENCODE_KERNEL<BITS, kBf16>), grid, dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((encode_kernel<BITS, kBf16>), grid, dim3(kThreads), 0, st,
                        (const uint8_t*)x, (uint8_t*)p, (int)ntiles);
-#undef QR_ENCODE_KERNEL
   return hipGetLastError() == hipSuccess ? QR_OK : QR_ERR_HIP;
 }
 
@@ -375,5 +346,11 @@ qr_status launch_reduce(int dt, const ReduceArgs& a, hipStream_t st) {
 qr_status launch_reduce_mixed_from3(int fmt_out, int dt, const ReduceArgs& a, hipStream_t st);
 qr_status launch_reduce_mixed_from4(int fmt_out, int dt, const ReduceArgs& a, hipStream_t st);
 qr_status launch_reduce_mixed_from8(int fmt_out, int dt, const ReduceArgs& a, hipStream_t st);
+// Asymmetric formats (qr_asym.hip, one object per input format): encode,
+// decode and the reduce into either asymmetric output format.
+qr_status launch_encode_asym(int fmt, int dt, const void* x, void* p, size_t ntiles, hipStream_t st);
+qr_status launch_decode_asym(int fmt, int dt, const void* p, void* y, size_t ntiles, hipStream_t st);
+qr_status launch_reduce_asym_from20(int fmt_out, int dt, const ReduceArgs& a, hipStream_t st);
+qr_status launch_reduce_asym_from24(int fmt_out, int dt, const ReduceArgs& a, hipStream_t st);
 
 }  // namespace qr

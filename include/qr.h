@@ -27,6 +27,22 @@
  *   INT8 tile (2176 B): 2048 code bytes, then 64 fp16 scales at byte 2048 + 2g
  *   decode: y = (code - Q) * d, exact in fp32, rounded to the I/O dtype.
  *
+ * Asymmetric group formats (the "Flash Communication" review of arXiv
+ * 2412.04964: fields pith_summary and key_machinery give asymmetric
+ * quantization with a scale and a zero point per group of 128; minor_comments
+ * on its Algorithm 1 give the dequantization (q - z) * s):
+ *   group  = 128 consecutive values, range [lo, hi] = [min(x, 0), max(x, 0)]
+ *   scale  s = fp16_RNE(min(fp32 (hi - lo) / (2^b - 1), 65504)),
+ *          e = fp32 1/s (0 if s == 0)
+ *   zero   z = clamp(round_half_even(-lo * e), 0, 2^b - 1)
+ *   code   q = clamp(round_half_even(x * e) + z, 0, 2^b - 1)
+ *   QR_ASYM4 tile (1072 B): 1024 B of 4-bit codes laid out as INT4, then 16
+ *            fp16 scales (group g at byte 1024 + 2g), then 16 uint8 zero
+ *            points (group g at byte 1056 + g)
+ *   QR_ASYM8 tile (2096 B): 2048 code bytes, 16 fp16 scales at 2048 + 2g,
+ *            16 zero points at 2080 + g
+ *   decode: y = (q - z) * s, exact in fp32, rounded to the I/O dtype.
+ *
  * Conventions for every call:
  *   - `n` counts values and must be a multiple of 2048 (QR_ERR_SIZE otherwise);
  *     n == 0 is a valid empty call that launches nothing and returns QR_OK.
@@ -60,7 +76,9 @@ typedef enum {
   QR_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
 } qr_status;
 
-typedef enum { QR_INT3 = 3, QR_INT4 = 4, QR_INT8 = 8 } qr_format;
+/* Symmetric 32-value block formats are named by their code width; the
+ * asymmetric 128-value group formats by 16 + code width. */
+typedef enum { QR_INT3 = 3, QR_INT4 = 4, QR_INT8 = 8, QR_ASYM4 = 20, QR_ASYM8 = 24 } qr_format;
 
 typedef enum { QR_FP16 = 0, QR_BF16 = 1 } qr_dtype;
 
@@ -68,7 +86,7 @@ typedef enum { QR_FP16 = 0, QR_BF16 = 1 } qr_dtype;
 #define QR_MAX_RANKS 16
 
 /* Bytes of the packed form of n values: n / 2048 tiles of 896 (INT3), 1152
- * (INT4) or 2176 (INT8) bytes.  Returns 0 for an unknown format or an n that
+ * (INT4), 2176 (INT8), 1072 (ASYM4) or 2096 (ASYM8) bytes.  Returns 0 for an unknown format or an n that
  * is not a multiple of 2048.  Tile sizes: "Design Highlights" (INT4 1152 B,
  * INT3 896 B per 2048-value per-rank tile). */
 size_t qr_packed_bytes(qr_format fmt, size_t n);
@@ -112,8 +130,10 @@ qr_status qr_reduce_compressed(qr_format fmt, qr_dtype dtype, const void *const 
  * decode) in fmt_out: mixed formats per phase, the "INT6" configuration of the
  * "Flash Communication" review (fields minor_comments, section 3.2.3, and
  * forward_implications: INT4 for the reduce-scatter inputs, INT8 for the
- * all-gather payload).  Any pair of INT3/INT4/INT8 is accepted;
- * qr_reduce_compressed(f, ...) is qr_reduce_compressed_mixed(f, f, ...).
+ * all-gather payload).  Any pair of INT3/INT4/INT8 is accepted, and any pair
+ * of ASYM4/ASYM8; a symmetric format paired with an asymmetric one is
+ * QR_ERR_UNSUPPORTED.  qr_reduce_compressed(f, ...) is
+ * qr_reduce_compressed_mixed(f, f, ...).
  *   packed_ranks  HOST array of R device pointers, qr_packed_bytes(fmt_in, n) each
  *   packed_out    device, qr_packed_bytes(fmt_out, n) bytes, written
  *   y_out         device, n values of `dtype`, written, or NULL

@@ -37,11 +37,14 @@ def test_packed_bytes(L):
     assert L.qr_packed_bytes(3, 2048) == 896
     assert L.qr_packed_bytes(4, 2048) == 1152
     assert L.qr_packed_bytes(8, 2048) == 2176
+    assert L.qr_packed_bytes(20, 2048) == 1072   # ASYM4: 1024 codes + 32 scales + 16 zero points
+    assert L.qr_packed_bytes(24, 2048) == 2096   # ASYM8: 2048 codes + 32 scales + 16 zero points
+    assert L.qr_packed_bytes(20, 2048 * 3) == 1072 * 3
     assert L.qr_packed_bytes(4, 2048 * 65536) == 1152 * 65536
     assert L.qr_packed_bytes(4, 0) == 0
     for bad_n in (1, 2047, 2049, 4096 + 32):
         assert L.qr_packed_bytes(4, bad_n) == 0
-    for bad_fmt in (0, 2, 5, 6, 16):
+    for bad_fmt in (0, 2, 5, 6, 16, 19, 21, 23, 25, 28):
         assert L.qr_packed_bytes(bad_fmt, 2048) == 0
 
 
@@ -143,3 +146,19 @@ def test_reduce_mixed_validation(L):
     assert redm(L, fi=8, fo=3, out=A + 2176 - 16) == qr.QR_ERR_ALIAS
     assert redm(L, fi=4, fo=3, ranks=[A], out=A - 896, y=0, n=0) == qr.QR_OK
     assert redm(L, n=0, ranks=[0], out=0, y=0) == qr.QR_OK
+
+
+def test_asym_validation(L):
+    """Asymmetric formats pass format validation; a symmetric format paired
+    with an asymmetric one is unsupported in either direction."""
+    assert enc(L, fmt=20, n=2047) == qr.QR_ERR_SIZE
+    assert enc(L, fmt=24, p=B + 2) == qr.QR_ERR_ALIGN
+    assert dec(L, fmt=20, y=0) == qr.QR_ERR_ARG
+    assert red(L, fmt=24, R=17) == qr.QR_ERR_ARG
+    for fi, fo in ((4, 20), (20, 4), (8, 24), (24, 3)):
+        assert redm(L, fi=fi, fo=fo) == qr.QR_ERR_UNSUPPORTED, (fi, fo)
+    # output sized by fmt_out: ASYM8 out (2096 B) 2048 B before an ASYM4 input overlaps it
+    assert redm(L, fi=20, fo=24, out=A - 2048) == qr.QR_ERR_ALIAS
+    assert redm(L, fi=20, fo=24, out=A + 1072 - 16) == qr.QR_ERR_ALIAS
+    assert redm(L, fi=24, fo=20, out=A + 2096 - 16) == qr.QR_ERR_ALIAS
+    assert redm(L, fi=20, fo=20, n=0, ranks=[0], out=0, y=0) == qr.QR_OK

@@ -21,7 +21,8 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 FMTS = ("int3", "int4", "int8")
-BITS = {"int3": 3, "int4": 4, "int8": 8}
+AFMTS = ("asym4", "asym8")
+BITS = {"int3": 3, "int4": 4, "int8": 8, "asym4": 20, "asym8": 24}   # oracle format ids
 DT = {"fp16": torch.float16, "bf16": torch.bfloat16}
 
 
@@ -215,7 +216,7 @@ def run_pipeline(qa, w, xs):
 def check_tiles(oracle, w, xs_host_tiles, packed, out, y, tiles):
     """Oracle on the given tiles of every rank vs the GPU's bytes there."""
     bits = BITS[w.fmt]
-    tb = P.tile_bytes(bits)
+    tb = oracle.packed_bytes(bits, 2048)
     idx_b = np.concatenate([np.arange(t * tb, (t + 1) * tb) for t in tiles])
     idx_v = np.concatenate([np.arange(t * 2048, (t + 1) * 2048) for t in tiles])
     nt = len(tiles) * 2048
@@ -226,7 +227,7 @@ def check_tiles(oracle, w, xs_host_tiles, packed, out, y, tiles):
         assert np.array_equal(y[idx_v], oracle.decode(bits, w.io_dtype, wr[0], nt))
         return
     obits = BITS[w.out_fmt]
-    otb = P.tile_bytes(obits)
+    otb = oracle.packed_bytes(obits, 2048)
     idx_o = np.concatenate([np.arange(t * otb, (t + 1) * otb) for t in tiles])
     wout, wy = oracle.reduce_mixed(bits, obits, w.io_dtype, wr, nt)
     assert np.array_equal(out[idx_o], wout), "re-encoded sum differs"
@@ -263,7 +264,7 @@ def test_workload_full_size_sampled(qa, oracle, name):
     ntiles = w.n // 2048
     rng = np.random.default_rng(ntiles)
     tiles = sorted(set([0, 1, ntiles - 1, ntiles // 2] + list(rng.integers(0, ntiles, 60))))
-    tb = P.tile_bytes(BITS[w.fmt])
+    tb = oracle.packed_bytes(BITS[w.fmt], 2048)
     sel_v = torch.tensor(np.concatenate([np.arange(t * 2048, (t + 1) * 2048) for t in tiles]), device="cuda")
     sel_b = np.concatenate([np.arange(t * tb, (t + 1) * tb) for t in tiles])
     xs_t = [u16(x[sel_v]) for x in xs]
@@ -338,3 +339,156 @@ def test_misaligned_and_aliased_device_buffers(qa):
         qa.qr_reduce_compressed("int4", torch.float16, [p[:1152]], 2048, packed_out=p[:1152], y_out=x[:2048])
     assert ei.value.status == 5
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# asymmetric group codec (128-value groups, scale + zero point)
+# ---------------------------------------------------------------------------
+
+def gen_groups(dtype, n, seed):
+    """Host fp16/bf16 bit patterns with one structure per 128-value group:
+    zero, one-signed (all positive / all negative), a range held by a single
+    32-value block (the group range crosses lanes), fp16-subnormal ranges
+    (zero-point clamp), huge magnitudes (scale saturation for bf16), a
+    shifted mean, and exact grid points (q - z) * 2^m."""
+    rng = np.random.default_rng(seed)
+    ng = n // 128
+    x = rng.standard_normal((ng, 128))
+    sel = rng.integers(0, 9, ng)
+    x[sel == 0] = 0.0
+    x[sel == 1] = np.abs(x[sel == 1]) * 3
+    x[sel == 2] = -np.abs(x[sel == 2]) * 0.3
+    k = int((sel == 3).sum())
+    if k:
+        x[sel == 3] *= 1e-3
+        lane = rng.integers(0, 4, k)
+        rows = np.nonzero(sel == 3)[0]
+        for r, l in zip(rows, lane):
+            x[r, 32 * l:32 * l + 32] *= 4000.0
+    k = int((sel == 4).sum())
+    if k:
+        x[sel == 4] = rng.integers(-400, 60, size=(k, 128)) * 2.0 ** -24
+    x[sel == 5] *= 2.0 ** 30 if dtype == "bf16" else 20000.0
+    x[sel == 6] = x[sel == 6] + 3.0
+    k = int((sel == 7).sum())
+    if k:
+        x[sel == 7] = (rng.integers(0, 16, size=(k, 128)) - 5) * 2.0 ** rng.integers(-8, 3, size=(k, 1))
+    x[sel == 8] = -0.0
+    x = x.ravel()
+    if dtype == "fp16":
+        return P.f16_bits(np.clip(x, -65504, 65504))
+    return P.bf16_bits(x.astype(np.float32).astype(np.float64))
+
+
+def agen(kind, dtype, n, seed):
+    return gen_groups(dtype, n, seed) if kind == "groups" else gen(kind, dtype, n, seed)
+
+
+def first_diff(got, want):
+    bad = np.nonzero(got != want)[0]
+    return bad[:8].tolist()
+
+
+@pytest.mark.parametrize("fmt", AFMTS)
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("ntiles", [1, 5, 37, 1031])
+@pytest.mark.parametrize("kind", ["normal", "outliers", "scales", "groups"])
+def test_asym_encode_decode_parity(qa, oracle, fmt, dtype, ntiles, kind):
+    n = ntiles * 2048
+    xb = agen(kind, dtype, n, seed=ntiles * 13 + len(kind))
+    log(f"asym encode/decode {fmt} {dtype} tiles={ntiles} {kind}")
+    p = qa.qr_encode(fmt, dev(xb, DT[dtype]))
+    y = qa.qr_decode(fmt, p, n, DT[dtype])
+    torch.cuda.synchronize()
+    want_p = oracle.encode(BITS[fmt], dtype, xb)
+    got_p = p.cpu().numpy()
+    assert got_p.size == want_p.size
+    assert np.array_equal(got_p, want_p), f"packed bytes differ at {first_diff(got_p, want_p)}"
+    assert np.array_equal(u16(y), oracle.decode(BITS[fmt], dtype, want_p, n))
+
+
+@pytest.mark.parametrize("fmt", AFMTS)
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_asym_decode_arbitrary_packed(qa, oracle, fmt, dtype):
+    """Decode of packed data no encoder produced: every code, zero points over
+    [0, 2^b - 1], every finite fp16 scale class (zero, subnormal, largest)."""
+    bits = 4 if fmt == "asym4" else 8
+    rng = np.random.default_rng(bits + 100)
+    T = 259
+    codes = rng.integers(0, 1 << bits, size=(T, 2048))
+    sb = rng.integers(0, 0x7C00, size=(T, 16)).astype(np.uint16)
+    sb[:, :3] = [0, 1, 0x7BFF]
+    zp = rng.integers(0, 1 << bits, size=(T, 16))
+    zp[:, :2] = [0, (1 << bits) - 1]
+    packed = P.asym_pack(bits, codes, sb, zp)
+    log(f"asym decode arbitrary {fmt} {dtype}")
+    y = qa.qr_decode(fmt, dev(packed), T * 2048, DT[dtype])
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(y), oracle.decode(BITS[fmt], dtype, packed, T * 2048))
+
+
+@pytest.mark.parametrize("fmt", AFMTS)
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 16])
+@pytest.mark.parametrize("ntiles", [3, 133])
+def test_asym_reduce_parity(qa, oracle, fmt, dtype, R, ntiles):
+    fid = BITS[fmt]
+    n = ntiles * 2048
+    kinds = ["normal", "groups", "scales", "outliers"]
+    xs = [agen(kinds[r % 4], dtype, n, seed=2000 * R + 10 * r + ntiles) for r in range(R)]
+    log(f"asym reduce {fmt} {dtype} R={R} tiles={ntiles}")
+    packed = [qa.qr_encode(fmt, dev(x, DT[dtype])) for x in xs]
+    out, y = qa.qr_reduce_compressed(fmt, DT[dtype], packed, n)
+    out2, none = qa.qr_reduce_compressed(fmt, DT[dtype], packed, n, with_output=False)
+    torch.cuda.synchronize()
+    assert none is None
+    wranks = [oracle.encode(fid, dtype, x) for x in xs]
+    for r in range(R):
+        assert np.array_equal(packed[r].cpu().numpy(), wranks[r]), r
+    wout, wy = oracle.reduce(fid, dtype, wranks, n)
+    got = out.cpu().numpy()
+    assert np.array_equal(got, wout), f"re-encoded tiles differ at {first_diff(got, wout)}"
+    assert np.array_equal(u16(y), wy)
+    assert np.array_equal(out2.cpu().numpy(), wout)
+
+
+@pytest.mark.parametrize("fi,fo", [("asym4", "asym8"), ("asym8", "asym4")])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("R", [1, 4, 8])
+def test_asym_reduce_mixed_parity(qa, oracle, fi, fo, dtype, R):
+    n = 37 * 2048
+    kinds = ["normal", "groups", "scales", "outliers"]
+    xs = [agen(kinds[r % 4], dtype, n, seed=91 * R + r) for r in range(R)]
+    log(f"asym reduce mixed {fi}->{fo} {dtype} R={R}")
+    packed = [qa.qr_encode(fi, dev(x, DT[dtype])) for x in xs]
+    out, y = qa.qr_reduce_compressed_mixed(fi, fo, DT[dtype], packed, n)
+    torch.cuda.synchronize()
+    assert out.numel() == oracle.packed_bytes(BITS[fo], n)
+    wout, wy = oracle.reduce_mixed(BITS[fi], BITS[fo], dtype,
+                                   [oracle.encode(BITS[fi], dtype, x) for x in xs], n)
+    assert np.array_equal(out.cpu().numpy(), wout)
+    assert np.array_equal(u16(y), wy)
+
+
+def test_asym_hand_built_groups(qa, oracle):
+    """Groups whose parameters are known by hand: the fp16 subnormal range that
+    clamps the zero point, the bf16 range that saturates the scale, and the
+    group minimum and maximum held by different lanes."""
+    for fmt, bits in (("asym4", 4), ("asym8", 8)):
+        qmax = (1 << bits) - 1
+        k = 22 if bits == 4 else 357
+        x16 = np.zeros(2048)
+        x16[0] = -k * 2.0 ** -24                 # group 0: z clamps to qmax, scale 2^-24
+        x16[128 + 5], x16[128 + 100] = -3.0, 5.0  # group 1: min in lane 4, max in lane 7
+        xb16 = P.f16_bits(x16)
+        xbf = np.zeros(2048)
+        xbf[0] = -2.0 ** 30                      # group 0: scale saturates at 65504, z = qmax
+        xbbf = P.bf16_bits(xbf)
+        log(f"asym hand-built groups {fmt}")
+        for dtype, xb, want_sb in (("fp16", xb16, 0x0001), ("bf16", xbbf, 0x7BFF)):
+            p = qa.qr_encode(fmt, dev(xb, DT[dtype]))
+            torch.cuda.synchronize()
+            got = p.cpu().numpy()
+            codes, sb, zp = P.asym_unpack(bits, got)
+            assert sb[0, 0] == want_sb and zp[0, 0] == qmax, (fmt, dtype)
+            assert np.array_equal(got, oracle.encode(BITS[fmt], dtype, xb)), (fmt, dtype)

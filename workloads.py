@@ -21,6 +21,10 @@ tiles):
                            independent per rank.
   int6_r8_fp16_32x1024x4096  the same inputs with the re-encoded sum in INT8
                            (INT4 reduce inputs + INT8 gather payload, "INT6").
+  asym4_r8_fp16_32x1024x4096  the same inputs through the asymmetric 4-bit
+                           group codec (128-value groups, scale + zero point).
+  asym6_r8_fp16_32x1024x4096  the same inputs, asymmetric 4-bit reduce inputs
+                           and an asymmetric 8-bit re-encoded sum.
 
 Random numbers come from torch's seeded generators (Philox on the GPU, the CPU
 generator on the host); each (seed, workload, rank) gets its own stream seed.
@@ -36,7 +40,7 @@ MIB = 1 << 20
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    fmt: str                 # "int3" | "int4" | "int8"
+    fmt: str                 # "int3" | "int4" | "int8" | "asym4" | "asym8"
     dtype: torch.dtype       # torch.float16 | torch.bfloat16
     ranks: int               # R simulated rank buffers (1 = encode/decode only)
     n: int                   # values per rank
@@ -83,6 +87,15 @@ WORKLOADS = {
                                           32 * 1024 * 4096, (32, 1024, 4096),
                                           channel_sigma=(0.01, 20.0), fmt_out="int8",
                                           data_key="int4_r8_fp16_32x1024x4096"),
+    # asymmetric group codec on the same activations
+    "asym4_r8_fp16_32x1024x4096": Workload("asym4_r8_fp16_32x1024x4096", "asym4", torch.float16, 8,
+                                           32 * 1024 * 4096, (32, 1024, 4096),
+                                           channel_sigma=(0.01, 20.0),
+                                           data_key="int4_r8_fp16_32x1024x4096"),
+    "asym6_r8_fp16_32x1024x4096": Workload("asym6_r8_fp16_32x1024x4096", "asym4", torch.float16, 8,
+                                           32 * 1024 * 4096, (32, 1024, 4096),
+                                           channel_sigma=(0.01, 20.0), fmt_out="asym8",
+                                           data_key="int4_r8_fp16_32x1024x4096"),
 }
 
 BENCH_WORKLOAD = "int4_r8_fp16_32x1024x4096"
