@@ -50,15 +50,17 @@ def algorithmic_bytes(w):
     return out
 
 
-def traffic_from_profiles(kernel):
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def traffic_from_profiles(kernel, workload):
     """Measured HBM bytes per launch from the committed counter summary, or None
-    when it is absent or was taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    if not os.path.exists(path):
+    when there is none for this workload or it was taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
-    with open(path) as f:
-        d = json.load(f)
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    with open(TRAFFIC_JSON) as f:
+        d = json.load(f).get(workload)
+    if not d or d.get("kernel_source_hash") != kernel_source_hash():
         return None
     return d.get("bytes_per_launch", {}).get(kernel)
 
@@ -71,8 +73,9 @@ def ingest_pmc(fetch_csv, write_csv, workload):
     """HBM bytes per launch of each kernel from two rocprofv3 counter runs
     (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of
     `bench.py --copy-ref --workload W`, each scaled so that the calibration copy
-    (n * 2 bytes read, n * 2 written) reads as its known size.  Written to
-    profiles/hbm_traffic.json with the hash of the kernel sources."""
+    (n * 2 bytes read, n * 2 written) reads as its known size.  Stored under
+    the workload's name in profiles/hbm_traffic.json with the hash of the
+    kernel sources."""
     import csv
     import statistics
 
@@ -99,15 +102,21 @@ def ingest_pmc(fetch_csv, write_csv, workload):
     known = w.n * 2
     f_scale = known / (fetch["copy"] * 1024)
     w_scale = known / (write["copy"] * 1024)
-    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+    out = {"kernel_source_hash": kernel_source_hash(),
            "fetch_scale": f_scale, "write_scale": w_scale,
            "fetch_kib_per_launch": fetch, "write_kib_per_launch": write,
            "bytes_per_launch": {k: round(fetch[k] * 1024 * f_scale + write[k] * 1024 * w_scale)
                                 for k in fetch if k in write and k != "copy"},
            "algorithmic_bytes_per_launch": {k: int(v) for k, v in algorithmic_bytes(w).items()}}
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    with open(path, "w") as f:
-        json.dump(out, f, indent=1)
+    allw = {}
+    if os.path.exists(TRAFFIC_JSON):
+        with open(TRAFFIC_JSON) as f:
+            allw = json.load(f)
+        if "kernel_source_hash" in allw:   # single-workload layout of older summaries
+            allw = {}
+    allw[workload] = out
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(allw, f, indent=1, sort_keys=True)
     print(json.dumps(out, indent=1))
 
 
@@ -288,7 +297,7 @@ def main():
     dom = max(kern_us, key=lambda k: kern_us[k] * launches[k])
     roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["achieved_gbs"],
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": kernels[dom]["frac"],
-                "traffic": traffic_from_profiles(dom)}
+                "traffic": traffic_from_profiles(dom, name)}
 
     result = {
         "metric": METRIC,

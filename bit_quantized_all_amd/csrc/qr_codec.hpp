@@ -85,6 +85,7 @@ struct Format<20> {
   static constexpr int kScaleOffset = 1024;
   static constexpr int kZeroOffset = 1056;
   static constexpr int kShift = 0;
+  static constexpr int kOddShift = 4;  // odd values decode as 16 (q - z)
 };
 template <>
 struct Format<24> {
@@ -95,6 +96,7 @@ struct Format<24> {
   static constexpr int kScaleOffset = 2048;
   static constexpr int kZeroOffset = 2080;
   static constexpr int kShift = 0;
+  static constexpr int kOddShift = 0;
 };
 
 // Packed codes of one 32-value block as held by its lane, by code width.
@@ -497,31 +499,48 @@ __device__ __forceinline__ uint32_t quantize_words_asym(const uint32_t (&w)[kBlo
   return params;
 }
 
-// Decodes one block of an asymmetric format into kk[i] = q_i - z (exact).
-//   4-bit: per byte (q + 128 - z) ^ 0x80 = q - z as int8 (q + 128 - z lies in
-//          [113, 143], so the byte-wise add never carries)
-//   8-bit: per 16-bit half q - z as int16 (packed subtract)
+// A 32-bit constant held in a VGPR, so that a three-operand bit operation can
+// take it together with a second constant (one scalar operand per VOP3).
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+  asm volatile("" : "+v"(c));
+  return c;
+}
+
+// Decodes one block of an asymmetric format into kk[i] = (q_i - z) * 2^(kOddShift
+// * (i & 1)), exactly; odd values then take the scale s * 2^-kOddShift.
+// The fp16 pattern 0x6400 | c is the value 1024 + c (c < 1024), so one
+// packed fp16 subtract gives two decoded codes at once, exactly (integers
+// below 2048), and the fp16 halves feed mixed-precision FMAs directly.
+//   4-bit: a unit word holds value j at bits 4j; masking 0x000F000F leaves
+//          values 0 and 4 as 1024 + q, masking 0x00F000F0 leaves values 1
+//          and 5 as 1024 + 16q (minus 1024 + 16z: 16(q - z)); the word
+//          shifted right by 8 gives values 2, 6 and 3, 7 the same way.
+//   8-bit: byte gathers put codes 0, 2 and 1, 3 of a word under a 0x64 byte.
 template <int F>
 __device__ __forceinline__ void decode_block_asym(const Block<F>& blk, uint32_t z, float (&kk)[kBlockValues]) {
+  // -(1024 + c) for an integer 0 <= c < 1024 is the fp16 pattern 0xE400 | c
+  const uint32_t nzb = 0xE400u | z;
+  const f16x2 nz = __builtin_bit_cast(f16x2, nzb | (nzb << 16));
   if constexpr (Format<F>::kCodeBits == 4) {
-    const uint32_t c = (0x80u - z) * 0x01010101u;
+    const uint32_t nzob = 0xE400u | (z << 4);
+    const f16x2 nzo = __builtin_bit_cast(f16x2, nzob | (nzob << 16));
+    const uint32_t m0 = vgpr_const(0x000F000Fu), m1 = vgpr_const(0x00F000F0u);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint32_t ev = ((blk.w[u] & 0x0F0F0F0Fu) + c) ^ 0x80808080u;         // values 8u + 2i
-      const uint32_t od = (((blk.w[u] >> 4) & 0x0F0F0F0Fu) + c) ^ 0x80808080u;  // values 8u + 2i + 1
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kk[8 * u + 2 * i] = sbyte(ev, i);
-        kk[8 * u + 2 * i + 1] = sbyte(od, i);
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t src = k < 2 ? blk.w[u] : blk.w[u] >> 8;
+        const uint32_t pat = (src & ((k & 1) ? m1 : m0)) | 0x64006400u;
+        const f16x2 h = __builtin_bit_cast(f16x2, pat) + ((k & 1) ? nzo : nz);
+        kk[8 * u + k] = (float)h.x;
+        kk[8 * u + k + 4] = (float)h.y;
       }
     }
   } else {
-    typedef short s16x2 __attribute__((ext_vector_type(2)));
-    const s16x2 zz = {(short)z, (short)z};
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-      const s16x2 ev = __builtin_bit_cast(s16x2, blk.w[w] & 0x00FF00FFu) - zz;         // values 4w, 4w + 2
-      const s16x2 od = __builtin_bit_cast(s16x2, (blk.w[w] >> 8) & 0x00FF00FFu) - zz;  // values 4w + 1, 4w + 3
+      const f16x2 ev = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, blk.w[w], 0x04020400u)) + nz;
+      const f16x2 od = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, blk.w[w], 0x04030401u)) + nz;
       kk[4 * w + 0] = (float)ev.x;
       kk[4 * w + 1] = (float)od.x;
       kk[4 * w + 2] = (float)ev.y;
@@ -552,8 +571,10 @@ __device__ __forceinline__ void st(T v, T* p) {
     *p = v;
 }
 
-// Codes of block g and its scale; for the asymmetric formats the scale and
-// zero point of the block's group (scale bits | zero point << 16).
+// Codes of block g and its scale.  For the asymmetric formats `scale`
+// receives one dword of the tile's 48-byte scale / zero-point region (dword
+// min(g & 15, 11)), and group_meta() later hands every lane its group's
+// values: one memory instruction instead of a 2-byte and a 1-byte load.
 template <int F, bool NT>
 __device__ __forceinline__ void load_block(const uint8_t* __restrict__ tile, int g, Block<F>& blk,
                                            uint32_t& scale) {
@@ -572,12 +593,23 @@ __device__ __forceinline__ void load_block(const uint8_t* __restrict__ tile, int
     blk.high = ld<NT>(reinterpret_cast<const uint32_t*>(tile + Format<3>::kHighOffset + 4 * g));
   }
   if constexpr (Format<F>::kAsym) {
-    const int grp = g >> 2;
-    scale = ld<NT>(reinterpret_cast<const uint16_t*>(tile + Format<F>::kScaleOffset + 2 * grp)) |
-            ((uint32_t)ld<NT>(tile + Format<F>::kZeroOffset + grp) << 16);
+    static_assert(Format<F>::kZeroOffset == Format<F>::kScaleOffset + 32, "scales then zero points");
+    const int j = (g & 15) < 11 ? (g & 15) : 11;
+    scale = ld<NT>(reinterpret_cast<const uint32_t*>(tile + Format<F>::kScaleOffset + 4 * j));
   } else {
     scale = ld<NT>(reinterpret_cast<const uint16_t*>(tile + Format<F>::kScaleOffset + 2 * g));
   }
+}
+
+// Scale bits | zero point << 16 of the group of lane g's block, from the
+// dwords load_block() left in the lanes: dwords 0..7 hold the 16 fp16 scales
+// (two each), dwords 8..11 the 16 zero points (four each).  Every lane of the
+// wave takes part (cross-lane permutes).
+__device__ __forceinline__ uint32_t group_meta(uint32_t m, int g) {
+  const int grp = g >> 2;
+  const uint32_t sdw = (uint32_t)__builtin_amdgcn_ds_bpermute((grp >> 1) << 2, (int)m);
+  const uint32_t zdw = (uint32_t)__builtin_amdgcn_ds_bpermute((8 + (grp >> 2)) << 2, (int)m);
+  return ((sdw >> (16 * (grp & 1))) & 0xffffu) | (((zdw >> (8 * (grp & 3))) & 0xffu) << 16);
 }
 
 // Stores block g; for the asymmetric formats the first lane of each group

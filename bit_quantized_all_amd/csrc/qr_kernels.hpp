@@ -148,17 +148,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint8_t* __restr
     uint32_t scale;
     load_block<BITS, QR_DEC_NT_LOAD>(packed + (size_t)tile * Format<BITS>::kTileBytes, lane, blk, scale);
     float kk[kBlockValues];
-    float dd;
+    float dd, ddo;  // scales of even and odd values
     if constexpr (Format<BITS>::kAsym) {
+      scale = group_meta(scale, lane);
       decode_block_asym<BITS>(blk, scale >> 16, kk);
       dd = scale_f32(scale);
+      ddo = dd * (1.0f / (1 << Format<BITS>::kOddShift));
     } else {
       decode_block<BITS>(blk, kk);
       dd = scale_f32(scale) * (1.0f / (1 << Format<BITS>::kShift));
+      ddo = dd;
     }
     float v[kBlockValues];
 #pragma unroll
-    for (int i = 0; i < kBlockValues; ++i) v[i] = kk[i] * dd;
+    for (int i = 0; i < kBlockValues; ++i) v[i] = kk[i] * ((i & 1) ? ddo : dd);
     write_lane_values<DT>(lds[wave], lane, v);
     flush_tile<QR_DEC_NT_STORE>(lds[wave], lane, y + (size_t)tile * (kTileValues * 2));
   }
@@ -198,20 +201,31 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float kk[kBlockValues];
-      float dd;
+      float dd, ddo;  // scales of even and odd values (exact products with kk)
       if constexpr (Format<BI>::kAsym) {
+        sc[r] = group_meta(sc[r], lane);
         decode_block_asym<BI>(blk[r], sc[r] >> 16, kk);
         dd = scale_f32(sc[r]);
+        ddo = dd * (1.0f / (1 << Format<BI>::kOddShift));
       } else {
         decode_block<BI>(blk[r], kk);
         dd = scale_f32(sc[r]) * kInvShift;
+        ddo = dd;
       }
       if (r == 0) {
+        // fma(k, d, +0) is the exact product k * d up to the sign of a zero
+        // (+0 for -0), which no later step can observe: it lets the fp16
+        // halves of the asymmetric decode feed one mixed-precision FMA
 #pragma unroll
-        for (int i = 0; i < kBlockValues; ++i) s[i] = kk[i] * dd;
+        for (int i = 0; i < kBlockValues; ++i) {
+          if constexpr (Format<BI>::kAsym)
+            s[i] = __builtin_fmaf(kk[i], (i & 1) ? ddo : dd, 0.0f);
+          else
+            s[i] = kk[i] * dd;
+        }
       } else {
 #pragma unroll
-        for (int i = 0; i < kBlockValues; ++i) s[i] = __builtin_fmaf(kk[i], dd, s[i]);
+        for (int i = 0; i < kBlockValues; ++i) s[i] = __builtin_fmaf(kk[i], (i & 1) ? ddo : dd, s[i]);
       }
     }
     // re-encode dtype_RNE(s): rounding is monotonic and symmetric, so the

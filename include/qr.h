@@ -41,7 +41,9 @@
  *            points (group g at byte 1056 + g)
  *   QR_ASYM8 tile (2096 B): 2048 code bytes, 16 fp16 scales at 2048 + 2g,
  *            16 zero points at 2080 + g
- *   decode: y = (q - z) * s, exact in fp32, rounded to the I/O dtype.
+ *   decode: y = (q - z) * s, exact in fp32, rounded to the I/O dtype.  A
+ *          zero point above 2^b - 1 is outside the format (the encoder never
+ *          writes one); decoding it gives unspecified values.
  *
  * Conventions for every call:
  *   - `n` counts values and must be a multiple of 2048 (QR_ERR_SIZE otherwise);
