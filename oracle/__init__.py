@@ -19,7 +19,7 @@ import numpy as np
 
 from . import build as _build
 
-FMT_BITS = {"int3": 3, "int4": 4, "int8": 8, "asym4": 20, "asym8": 24}
+FMT_BITS = {"int3": 3, "int4": 4, "int8": 8, "asym4": 20, "asym8": 24, "fp4": 36}
 DTYPES = {"fp16": 0, "bf16": 1}
 TILE = 2048
 BLOCK = 32

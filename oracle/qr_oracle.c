@@ -54,6 +54,17 @@
  *      0, 2^b - 1); decode (q - z) * s, exact in fp32.  A tile of 2048 values
  *      is [codes (as INT4 / INT8) | 16 fp16 scales | 16 uint8 zero points]:
  *      1072 bytes for 4-bit codes, 2096 for 8-bit.
+ *  R8  FP4 block codec ([QR] introduction: a hardware-accelerated FP4 path on
+ *      MI355 that is interchangeable with INT4; the page gives no format): the
+ *      element is OCP MX FP4 E2M1 (bit 3 sign, bits 2..1 exponent with bias 1,
+ *      bit 0 mantissa; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no inf or NaN),
+ *      in INT4's framework: blocks of 32 values with one fp16 scale, codes
+ *      packed as INT4 nibbles, a 1152-byte tile [1024 B codes | 128 B scales].
+ *      d = fp16_RNE(min(RN32(m / 6), 65504)) (the block maximum maps to the
+ *      largest magnitude 6); e = RN32(1 / d) (0 when d == 0); the code of x is
+ *      the E2M1 value nearest to RN32(x * e), ties to an even mantissa,
+ *      magnitudes above 6 saturating to 6, the sign kept (so a negative value
+ *      that rounds to zero is -0, code 8); decode = value * d, exact in fp32.
  *
  * All floating point is IEEE binary32 with round-to-nearest-even; build with
  * -O2 -ffp-contract=off and without -ffast-math.
@@ -156,14 +167,18 @@ static uint16_t f32_to_dtype(int dtype, float x) {
 /* ------------------------------------------------------------------------ */
 
 /* Format ids: 3, 4, 8 = symmetric block codec with that many bits; 20, 24 =
-   asymmetric group codec with 4 or 8 bits (R7). */
+   asymmetric group codec with 4 or 8 bits (R7); 36 = FP4 E2M1 block codec
+   (R8), laid out like INT4. */
 #define QRO_ASYM 16
+#define QRO_FP4 36
 static int fmt_bits(int fmt) {
   if (fmt == 3 || fmt == 4 || fmt == 8) return fmt;
   if (fmt == QRO_ASYM + 4 || fmt == QRO_ASYM + 8) return fmt - QRO_ASYM;
+  if (fmt == QRO_FP4) return 4;
   return 0;
 }
-static int fmt_asym(int fmt) { return fmt > QRO_ASYM; }
+static int fmt_asym(int fmt) { return fmt == QRO_ASYM + 4 || fmt == QRO_ASYM + 8; }
+static int fmt_fp4(int fmt) { return fmt == QRO_FP4; }
 
 #define QRO_AGROUP 128 /* values per asymmetric group (R7) */
 #define QRO_AGROUPS (QRO_TILE / QRO_AGROUP)
@@ -368,16 +383,74 @@ static float decode_value_asym(int bits, const uint8_t *tile, int i) {
   return (float)((int)get_code(bits, tile, i) - z) * d;
 }
 
+/* ------------------------------------------------------------------------ */
+/* FP4 E2M1 block codec (R8)                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Value of an E2M1 code: exponent field 0 holds 0 and the subnormal 0.5
+   (mantissa * 2^-1); fields 1..3 hold (1 + mantissa / 2) * 2^(field - 1). */
+static float fp4_value(unsigned code) {
+  int ef = (code >> 1) & 3, m = code & 1;
+  float mag = ef == 0 ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, ef - 1);
+  return (code & 8u) ? -mag : mag;
+}
+
+/* Code of the E2M1 value nearest to v: round to nearest, ties to even, at the
+   spacing of v's binade (0.5 below 2, 1 in [2, 4), 2 from 4 on), then
+   saturate magnitudes above 6; the sign bit is v's sign. */
+static unsigned fp4_code(float v) {
+  float a = fabsf(v);
+  float step = a < 2.0f ? 0.5f : (a < 4.0f ? 1.0f : 2.0f);
+  float r = rintf(a / step) * step; /* exact: the step is a power of two */
+  if (r > 6.0f) r = 6.0f;
+  unsigned mc = 0;
+  while (mc < 7 && fp4_value(mc) != r) ++mc; /* r is one of the eight magnitudes */
+  return (signbit(v) ? 8u : 0u) | mc;
+}
+
+/* Scale of an FP4 block with absolute maximum m: the maximum maps to 6. */
+void qro_fp4_block_scale(float m, uint16_t *d_bits, float *e) {
+  float t = m / 6.0f;             /* correctly rounded binary32 quotient */
+  if (t > 65504.0f) t = 65504.0f; /* saturate at the largest binary16 */
+  *d_bits = qro_f32_to_f16(t);
+  float d = qro_f16_to_f32(*d_bits);
+  *e = (d == 0.0f) ? 0.0f : 1.0f / d; /* FP4 multiplier */
+}
+
+static void encode_tile_fp4(const float *x, uint8_t *tile) {
+  memset(tile, 0, tile_bytes(4));
+  for (int g = 0; g < QRO_BLOCKS; ++g) {
+    const float *xb = x + g * QRO_BLOCK;
+    float m = 0.0f;
+    for (int i = 0; i < QRO_BLOCK; ++i)
+      if (fabsf(xb[i]) > m) m = fabsf(xb[i]);
+    uint16_t d_bits;
+    float e;
+    qro_fp4_block_scale(m, &d_bits, &e);
+    for (int i = 0; i < QRO_BLOCK; ++i) put_code(4, tile, g * QRO_BLOCK + i, fp4_code(xb[i] * e));
+    put_scale(4, tile, g, d_bits);
+  }
+}
+
+/* value * d is exact in binary32 (2 and 11 significant bits). */
+static float decode_value_fp4(const uint8_t *tile, int i) {
+  return fp4_value(get_code(4, tile, i)) * qro_f16_to_f32(get_scale(4, tile, i / QRO_BLOCK));
+}
+
 /* Format-generic tile encode / value decode. */
 static void encode_tile_fmt(int fmt, const float *x, uint8_t *tile) {
   if (fmt_asym(fmt))
     encode_tile_asym(fmt_bits(fmt), x, tile);
+  else if (fmt_fp4(fmt))
+    encode_tile_fp4(x, tile);
   else
     encode_tile(fmt_bits(fmt), x, tile);
 }
 
 static float decode_value_fmt(int fmt, const uint8_t *tile, int i) {
-  return fmt_asym(fmt) ? decode_value_asym(fmt_bits(fmt), tile, i) : decode_value(fmt_bits(fmt), tile, i);
+  if (fmt_asym(fmt)) return decode_value_asym(fmt_bits(fmt), tile, i);
+  if (fmt_fp4(fmt)) return decode_value_fp4(tile, i);
+  return decode_value(fmt_bits(fmt), tile, i);
 }
 
 /* ------------------------------------------------------------------------ */

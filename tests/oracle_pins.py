@@ -1073,6 +1073,224 @@ def pin_asym_zero_point_clamp(o):
 
 
 
+# ---------------------------------------------------------------------------
+# FP4 E2M1 block codec (format id 36, laid out like INT4)
+# ---------------------------------------------------------------------------
+
+FP4 = 36
+FP4_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def fp4_nearest(v):
+    """E2M1 code nearest to each float64 v by brute-force distance over the
+    eight magnitudes, a tie going to the code with an even mantissa bit;
+    magnitudes above 6 take 6; the sign bit is v's sign (-0 and negative
+    values that round to zero give code 8)."""
+    v = np.asarray(v, np.float64)
+    a = np.minimum(np.abs(v), 6.0)
+    dist = np.abs(a[:, None] - FP4_MAG[None, :])
+    best = dist.min(axis=1, keepdims=True)
+    cand = dist == best
+    even = cand & (np.arange(8)[None, :] % 2 == 0)
+    pick = np.where(even.any(axis=1), np.argmax(even, axis=1), np.argmax(cand, axis=1))
+    return pick + 8 * np.signbit(v)
+
+
+def pin_fp4_value_table(o):
+    """Decoding codes 0..15 with scale 1.0 gives the E2M1 values of the OCP MX
+    specification (golden fp4_e2m1_values.txt); the code sits in the INT4
+    nibble order and the scale in the INT4 scale slot."""
+    rows = read_golden("fp4_e2m1_values.txt")
+    want = {int(r[0]): float(r[4]) for r in rows}
+    neg_zero = {int(r[0]) for r in rows if r[4] == "-0"}
+    codes = np.tile(np.arange(16), 2048 // 16).reshape(1, 2048)
+    sb = np.full((1, 64), 0x3C00, np.uint16)
+    y = o.decode_f32(FP4, pack(4, codes, sb), 2048)
+    for i in range(32):
+        c = int(codes[0, i])
+        assert y[i] == want[c], (c, y[i], want[c])
+        assert np.signbit(y[i]) == (c in neg_zero or want[c] < 0), c
+    assert o.packed_bytes(FP4, 2048) == 1152
+
+
+def _fp4_blocks(anchor, xs):
+    """Blocks [anchor, x, 0, ...] as fp16 bits, padded to whole tiles."""
+    nb = xs.size
+    blocks = np.zeros((nb, BLOCK), np.uint16)
+    blocks[:, 0] = f16_bits(anchor)
+    blocks[:, 1] = f16_bits(xs)
+    return pad_tiles(blocks), nb
+
+
+def pin_fp4_bruteforce_pow2(o):
+    """Blocks [6 * 2^k, x, 0...]: the scale is 2^k exactly (6 * 2^k / 6) and
+    the code of every finite fp16 x with |x| <= 6 * 2^k is the E2M1 value
+    nearest to x / 2^k (brute-force distance, ties to an even mantissa,
+    sign kept), for exponents k covering normal and subnormal fp16 scales;
+    decode gives that value times 2^k."""
+    allb, allv = all_finite("fp16")
+    for k in (-24, -20, -14, -6, -1, 0, 3, 12):
+        a = 6.0 * 2.0 ** k
+        if f16_value(f16_bits(a)) != a:
+            continue
+        sel = np.abs(allv) <= a
+        xv = allv[sel]
+        p, nb = _fp4_blocks(a, xv)
+        codes, sb = unpack(4, o.encode(FP4, "fp16", p))
+        codes = codes.reshape(-1, BLOCK)[:nb]
+        assert np.all(sb.ravel()[:nb] == pow2_f16_bits(k)), k
+        want = fp4_nearest(xv / 2.0 ** k)
+        bad = codes[:, 1] != want
+        assert not bad.any(), (k, xv[bad][:4], codes[bad, 1][:4], want[bad][:4])
+        assert np.all(codes[:, 0] == 7), k
+        y = o.decode_f32(FP4, o.encode(FP4, "fp16", p), p.size).reshape(-1, BLOCK)[:nb, 1]
+        vals = np.where(want >= 8, -FP4_MAG[want % 8], FP4_MAG[want % 8]) * 2.0 ** k
+        assert np.array_equal(y.astype(np.float64), vals), k
+
+
+def pin_fp4_general_scale(o):
+    """Non-power-of-two scales d with 6 * d exact in fp16: the scale is d and
+    the code of every fp16 x in range is the nearest E2M1 value to
+    RN32(x * RN32(1/d)) (products in float64, rounded once).  Some x round
+    differently under x / d, so the pin separates multiplying by the fp32
+    reciprocal from dividing by the scale."""
+    allb, allv = all_finite("fp16")
+    diff_seen = 0
+    for d_bits in (0x3555, 0x2E66, 0x3A00, 0x0F90, 0x3300, 0x3368, 0x17A8, 0x3480):
+        d = float(f16_value(np.uint16(d_bits)))
+        a = 6.0 * d
+        if f16_value(f16_bits(a)) != a:
+            continue
+        xv = allv[np.abs(allv) <= a]
+        p, nb = _fp4_blocks(a, xv)
+        codes, sb = unpack(4, o.encode(FP4, "fp16", p))
+        codes = codes.reshape(-1, BLOCK)[:nb]
+        assert np.all(sb.ravel()[:nb] == d_bits), hex(d_bits)
+        e = np.float64(np.float32(1.0 / d))
+        v = (xv * e).astype(np.float32).astype(np.float64)
+        want = fp4_nearest(v)
+        bad = codes[:, 1] != want
+        assert not bad.any(), (hex(d_bits), xv[bad][:4], codes[bad, 1][:4], want[bad][:4])
+        diff_seen += int((fp4_nearest((xv / d).astype(np.float32).astype(np.float64)) != want).sum())
+    assert diff_seen > 0
+
+
+def pin_fp4_scale_every_max(o):
+    """For every positive finite fp16 block maximum m (block [m, 0, ...]): the
+    scale is fp16(RN32(m / 6)), the quotient taken in float64 and rounded once
+    to float32 (harmless double rounding: 53 >= 2 * 24 + 2) and then to fp16;
+    the maximum itself codes as 6 (or saturates).  (m * RN32(1/6) differs from
+    RN32(m / 6) for about a third of the m, by one fp32 ulp, but never after
+    the rounding to fp16, for any fp16 or bf16 m: the two readings give the
+    same scale, so no planted mistake can separate them.)"""
+    m_bits = np.arange(1, 0x7C00, dtype=np.uint16)
+    m = f16_value(m_bits).astype(np.float64)
+    p, nb = _fp4_blocks(0.0, np.zeros(0))
+    blocks = np.zeros((m.size, BLOCK), np.uint16)
+    blocks[:, 0] = m_bits
+    codes, sb = unpack(4, o.encode(FP4, "fp16", pad_tiles(blocks)))
+    t = (m / 6.0).astype(np.float32)
+    want = f16_bits(np.minimum(t.astype(np.float64), 65504.0))
+    got = sb.ravel()[:m.size]
+    assert np.array_equal(got, want), np.argwhere(got != want)[:4].ravel().tolist()
+    d = f16_value(got).astype(np.float64)
+    ok = d > 0
+    e = (1.0 / d[ok]).astype(np.float32).astype(np.float64)
+    v = (m[ok] * e).astype(np.float32).astype(np.float64)
+    assert np.array_equal(codes.reshape(-1, BLOCK)[:m.size, 0][ok], fp4_nearest(v))
+
+
+def pin_fp4_zero_and_saturation(o):
+    """Zero and -0 blocks: scale 0, codes 0 and 8 (sign kept), decode +-0.
+    A bf16 block whose maximum exceeds 6 * 65504: the scale saturates at
+    65504 (0x7BFF) and values beyond 6 * 65504 code as +-6 (7 / 15)."""
+    for dtype in DTYPES:
+        x = np.zeros(2048)
+        x[32:64:2] = -0.0
+        x[64:96] = 0.0
+        x[64] = -2.0 ** -100 if dtype == "bf16" else 0.0   # scale rounds to 0: x * 0 = -0
+        codes, sb = unpack(4, o.encode(FP4, dtype, dtype_bits(dtype, x)))
+        assert sb[0, 0] == 0 and sb[0, 1] == 0 and np.all(codes[0, :32] == 0)
+        assert np.all(codes[0, 32:64:2] == 8) and np.all(codes[0, 33:64:2] == 0)
+        if dtype == "bf16":
+            assert codes[0, 64] == 8
+    xb = np.zeros(2048)
+    xb[:4] = [2.0 ** 30, -2.0 ** 30, 3.0 * 65504, -1.0]
+    codes, sb = unpack(4, o.encode(FP4, "bf16", bf16_bits(xb)))
+    assert sb[0, 0] == 0x7BFF
+    assert codes[0, 0] == 7 and codes[0, 1] == 15
+    assert codes[0, 2] == fp4_nearest([float(np.float32(np.float32(bf16_value(bf16_bits(3.0 * 65504))) * np.float32(1 / 65504.0)))])[0]
+
+
+def pin_fp4_reduce_exact(o, seed=31):
+    """Two ranks whose blocks share the scale s (a 6 * s anchor in each, at
+    positions where the other rank is 0) and whose element pairs sum to E2M1
+    values: the re-encoded sum has scale s, the exact codes, and decodes to
+    the exact sum."""
+    rng = np.random.default_rng(seed)
+    pairs = [(0.5, 0.5, 1.0), (1, 1, 2), (1.5, 1.5, 3), (2, 2, 4), (3, 3, 6), (0.5, 1, 1.5),
+             (-1, 3, 2), (4, -1, 3), (-2, -1, -3), (-0.5, -1, -1.5), (2, -6, -4), (0, 0, 0), (6, -6, 0)]
+    for dtype in DTYPES:
+        nb = 64
+        a = np.zeros((nb, BLOCK)); b = np.zeros((nb, BLOCK)); tot = np.zeros((nb, BLOCK))
+        idx = rng.integers(0, len(pairs), size=(nb, BLOCK))
+        for j, (pa, pb, pt) in enumerate(pairs):
+            a[idx == j], b[idx == j], tot[idx == j] = pa, pb, pt
+        a[:, 0], b[:, 0], tot[:, 0] = 6, 0, 6
+        a[:, 1], b[:, 1], tot[:, 1] = 0, 6, 6
+        s = 2.0 ** rng.integers(-8, 3, size=nb)
+        ra = o.encode(FP4, dtype, dtype_bits(dtype, (a * s[:, None]).ravel()))
+        rb = o.encode(FP4, dtype, dtype_bits(dtype, (b * s[:, None]).ravel()))
+        out, y = o.reduce(FP4, dtype, [ra, rb], nb * BLOCK)
+        codes, sb = unpack(4, out)
+        assert np.array_equal(sb.ravel(), f16_bits(s)), dtype
+        assert np.array_equal(codes.reshape(nb, BLOCK), fp4_nearest(tot.ravel()).reshape(nb, BLOCK)), dtype
+        assert np.array_equal(y, dtype_bits(dtype, (tot * s[:, None]).ravel())), dtype
+
+
+def _fp4_exact(codes, sb):
+    """Exact decode in float64 from the E2M1 magnitudes and the block scales."""
+    c = np.asarray(codes).reshape(-1, 64, BLOCK)
+    mag = FP4_MAG[c % 8] * f16_value(sb)[:, :, None]
+    return np.where(c >= 8, -mag, mag).ravel()
+
+
+def pin_fp4_reduce_r1_composition(o, seed=32):
+    """R = 1: the reduce re-encodes dtype_RNE(exact decode) and decodes it; the
+    exact decode and the dtype rounding are computed here in numpy / torch
+    from the codes and scales."""
+    rng = np.random.default_rng(seed)
+    for dtype in DTYPES:
+        n = 2 * TILE
+        xb = _rng_blocks(rng, dtype, n // BLOCK)
+        p = o.encode(FP4, dtype, xb)
+        codes, sb = unpack(4, p)
+        zb = dtype_bits(dtype, _fp4_exact(codes, sb))
+        out, y = o.reduce(FP4, dtype, [p], n)
+        assert np.array_equal(out, o.encode(FP4, dtype, zb)), dtype
+        c2, s2 = unpack(4, out)
+        assert np.array_equal(y, dtype_bits(dtype, _fp4_exact(c2, s2))), dtype
+
+
+def pin_fp4_error_bound(o, seed=33):
+    """|decode(encode(x)) - x| is at most half the E2M1 spacing at x / d (0.25,
+    0.5 or 1 times d) plus the effect of the rounded scale, per value; the
+    bound is reached to within 10% on random data (not vacuous)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(64 * 2048)
+    xb = f16_bits(x)
+    xv = f16_value(xb).astype(np.float64)
+    p = o.encode(FP4, "fp16", xb)
+    codes, sb = unpack(4, p)
+    d = np.repeat(f16_value(sb.ravel()).astype(np.float64), 32)
+    y = o.decode_f32(FP4, p, x.size).astype(np.float64)
+    a = np.abs(xv) / d
+    half = np.where(a < 2, 0.25, np.where(a < 4, 0.5, 1.0))
+    bound = half * d + np.abs(xv) * 2.0 ** -10 + 1e-30
+    err = np.abs(y - xv)
+    assert np.all(err <= bound), float((err / bound).max())
+    assert (err / bound).max() > 0.9
+
 ALL_PINS = [
     pin_tile_bytes,
     pin_unit_bit_order,
@@ -1104,5 +1322,13 @@ ALL_PINS = [
     pin_asym_overflow_sum,
     pin_asym_error_bound,
     pin_error_bound,
+    pin_fp4_value_table,
+    pin_fp4_bruteforce_pow2,
+    pin_fp4_general_scale,
+    pin_fp4_scale_every_max,
+    pin_fp4_zero_and_saturation,
+    pin_fp4_reduce_exact,
+    pin_fp4_reduce_r1_composition,
+    pin_fp4_error_bound,
 ]
 

@@ -108,6 +108,21 @@ MUTANTS = [
     ("asym: zero point truncated", [("float zf = rintf(-lo * *e);", "float zf = truncf(-lo * *e);")]),
     ("asym: no clamp at the top", [("k = fminf(fmaxf(k, 0.0f), (float)qmax);", "k = fmaxf(k, 0.0f);")]),
     ("asym: rounding after the zero point", [("float k = rintf(u) + (float)*z;", "float k = rintf(u + (float)*z);")]),
+    ("fp4: ties away from zero", [("float r = rintf(a / step) * step; /* exact: the step is a power of two */",
+                                  "float r = roundf(a / step) * step;")]),
+    ("fp4: truncation", [("float r = rintf(a / step) * step; /* exact: the step is a power of two */",
+                          "float r = floorf(a / step) * step;")]),
+    ("fp4: saturation at 4", [("if (r > 6.0f) r = 6.0f;", "if (r > 4.0f) r = 4.0f;")]),
+    ("fp4: maximum mapped to 4", [("float t = m / 6.0f; ", "float t = m / 4.0f; ")]),
+    ("fp4: sign of zero dropped", [("return (signbit(v) ? 8u : 0u) | mc;", "return (v < 0.0f ? 8u : 0u) | mc;")]),
+    ("fp4: exponent bias 2", [("ldexpf(1.0f + 0.5f * (float)m, ef - 1)", "ldexpf(1.0f + 0.5f * (float)m, ef - 2)")]),
+    ("fp4: no subnormal", [("ef == 0 ? 0.5f * (float)m :", "ef == 0 ? 0.0f * (float)m :")]),
+    ("fp4: uniform step 0.5", [("float step = a < 2.0f ? 0.5f : (a < 4.0f ? 1.0f : 2.0f);", "float step = 0.5f;")]),
+    ("fp4: divide by the scale", [("fp4_code(xb[i] * e)", "fp4_code(e == 0.0f ? 0.0f * xb[i] : xb[i] / qro_f16_to_f32(d_bits))")]),
+    ("fp4: scale not saturated", [("if (t > 65504.0f) t = 65504.0f; /* saturate at the largest binary16 */", "")]),
+    ("fp4: multiplier rounded to fp16", [("*e = (d == 0.0f) ? 0.0f : 1.0f / d; /* FP4 multiplier */",
+                                          "*e = (d == 0.0f) ? 0.0f : qro_f16_to_f32(qro_f32_to_f16(1.0f / d));")]),
+    ("fp4: decoded as INT4", [("if (fmt_fp4(fmt)) return decode_value_fp4(tile, i);", "")]),
     ("asym: groups of 64", [("#define QRO_AGROUP 128 ", "#define QRO_AGROUP 64 ")]),
 ]
 
