@@ -27,8 +27,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GB/s of FP16 input through encode+compressed-reduce+decode; % HBM peak"
 PEAK_HBM_GBS = 8000.0
-TILE_BYTES = {"int3": 896, "int4": 1152, "int8": 2176, "asym4": 1072, "asym8": 2096}
-FORMAT_IDS = {"int3": 3, "int4": 4, "int8": 8, "asym4": 20, "asym8": 24}
+TILE_BYTES = {"int3": 896, "int4": 1152, "int8": 2176, "asym4": 1072, "asym8": 2096, "fp4": 1152}
+FORMAT_IDS = {"int3": 3, "int4": 4, "int8": 8, "asym4": 20, "asym8": 24, "fp4": 36}
 KERNEL_SOURCES = ["bit_quantized_all_amd/csrc/qr_kernels.hpp", "bit_quantized_all_amd/csrc/qr_codec.hpp"]
 
 

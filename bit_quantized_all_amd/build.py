@@ -16,7 +16,8 @@ _CSRC = os.path.join(HERE, "csrc")
 # per input format
 SOURCES = [(os.path.join(_CSRC, "qr_api.hip"), [])] + [
     (os.path.join(_CSRC, "qr_reduce_mixed.hip"), [f"-DQR_MIXED_IN={b}"]) for b in (3, 4, 8)] + [
-    (os.path.join(_CSRC, "qr_asym.hip"), [f"-DQR_ASYM_IN={f}"]) for f in (20, 24)]
+    (os.path.join(_CSRC, "qr_asym.hip"), [f"-DQR_ASYM_IN={f}"]) for f in (20, 24)] + [
+    (os.path.join(_CSRC, "qr_fp4.hip"), [])]
 LIB = os.path.join(HERE, "libqr.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -60,13 +61,13 @@ def build(out=LIB, extra=(), quiet=True, sources=None):
     return out
 
 
-TEST_HELPER_SRC = os.path.join(ROOT, "tests", "gpu_helpers", "scale_check.hip")
+TEST_HELPER_SRCS = [os.path.join(ROOT, "tests", "gpu_helpers", f) for f in ("scale_check.hip", "fp4_check.hip")]
 TEST_HELPER_LIB = os.path.join(ROOT, "tests", "gpu_helpers", "libscale_check.so")
 
 
 def build_test_helpers(quiet=True):
     """Test-only HIP helper that exercises the codec's device functions directly."""
-    return build(out=TEST_HELPER_LIB, sources=[TEST_HELPER_SRC], quiet=quiet)
+    return build(out=TEST_HELPER_LIB, sources=TEST_HELPER_SRCS, quiet=quiet)
 
 
 if __name__ == "__main__":

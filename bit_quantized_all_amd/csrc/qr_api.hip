@@ -21,6 +21,7 @@ inline int tile_bytes(int fmt) {
     case QR_INT8: return Format<8>::kTileBytes;
     case QR_ASYM4: return Format<20>::kTileBytes;
     case QR_ASYM8: return Format<24>::kTileBytes;
+    case QR_FP4: return Format<36>::kTileBytes;
     default: return 0;
   }
 }
@@ -62,6 +63,7 @@ qr_status qr_encode(qr_format fmt, qr_dtype dtype, const void* x, void* packed, 
   switch (fmt) {
     case QR_ASYM4:
     case QR_ASYM8: return launch_encode_asym(fmt, dtype, x, packed, nt, st);
+    case QR_FP4: return launch_encode_fp4(dtype, x, packed, nt, st);
     case QR_INT3: return launch_encode<3>(dtype, x, packed, nt, st);
     case QR_INT4: return launch_encode<4>(dtype, x, packed, nt, st);
     default: return launch_encode<8>(dtype, x, packed, nt, st);
@@ -81,6 +83,7 @@ qr_status qr_decode(qr_format fmt, qr_dtype dtype, const void* packed, void* y, 
   switch (fmt) {
     case QR_ASYM4:
     case QR_ASYM8: return launch_decode_asym(fmt, dtype, packed, y, nt, st);
+    case QR_FP4: return launch_decode_fp4(dtype, packed, y, nt, st);
     case QR_INT3: return launch_decode<3>(dtype, packed, y, nt, st);
     case QR_INT4: return launch_decode<4>(dtype, packed, y, nt, st);
     default: return launch_decode<8>(dtype, packed, y, nt, st);
@@ -91,7 +94,7 @@ qr_status qr_reduce_compressed_mixed(qr_format fmt_in, qr_format fmt_out, qr_dty
                                      const void* const* packed_ranks, int R, void* packed_out, void* y_out,
                                      size_t n, void* stream) {
   if (!tile_bytes(fmt_in) || !tile_bytes(fmt_out) || (dtype != QR_FP16 && dtype != QR_BF16) ||
-      is_asym(fmt_in) != is_asym(fmt_out))
+      is_asym(fmt_in) != is_asym(fmt_out) || (fmt_in == QR_FP4) != (fmt_out == QR_FP4))
     return QR_ERR_UNSUPPORTED;
   if (R < 1 || R > QR_MAX_RANKS) return QR_ERR_ARG;
   if (n % kTileValues || too_large(n)) return QR_ERR_SIZE;
@@ -118,6 +121,7 @@ qr_status qr_reduce_compressed_mixed(qr_format fmt_in, qr_format fmt_out, qr_dty
   hipStream_t st = (hipStream_t)stream;
   if (fmt_in == QR_ASYM4) return launch_reduce_asym_from20(fmt_out, dtype, a, st);
   if (fmt_in == QR_ASYM8) return launch_reduce_asym_from24(fmt_out, dtype, a, st);
+  if (fmt_in == QR_FP4) return launch_reduce_fp4(dtype, a, st);
   if (fmt_in != fmt_out) {
     switch (fmt_in) {
       case QR_INT3: return launch_reduce_mixed_from3(fmt_out, dtype, a, st);

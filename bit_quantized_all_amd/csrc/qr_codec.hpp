@@ -51,6 +51,7 @@ struct Format;
 template <>
 struct Format<3> {
   static constexpr bool kAsym = false;
+  static constexpr bool kFp4 = false;
   static constexpr int kCodeBits = 3;
   static constexpr int kQ = 4;
   static constexpr int kTileBytes = 896;   // 512 (2-bit plane) + 256 (1-bit plane) + 128
@@ -61,6 +62,7 @@ struct Format<3> {
 template <>
 struct Format<4> {
   static constexpr bool kAsym = false;
+  static constexpr bool kFp4 = false;
   static constexpr int kCodeBits = 4;
   static constexpr int kQ = 8;
   static constexpr int kTileBytes = 1152;  // 1024 + 128
@@ -70,6 +72,7 @@ struct Format<4> {
 template <>
 struct Format<8> {
   static constexpr bool kAsym = false;
+  static constexpr bool kFp4 = false;
   static constexpr int kCodeBits = 8;
   static constexpr int kQ = 128;
   static constexpr int kTileBytes = 2176;  // 2048 + 128
@@ -79,6 +82,7 @@ struct Format<8> {
 template <>
 struct Format<20> {
   static constexpr bool kAsym = true;
+  static constexpr bool kFp4 = false;
   static constexpr int kCodeBits = 4;
   static constexpr int kQmax = 15;
   static constexpr int kTileBytes = 1072;  // 1024 codes + 16 fp16 scales + 16 zero points
@@ -90,6 +94,7 @@ struct Format<20> {
 template <>
 struct Format<24> {
   static constexpr bool kAsym = true;
+  static constexpr bool kFp4 = false;
   static constexpr int kCodeBits = 8;
   static constexpr int kQmax = 255;
   static constexpr int kTileBytes = 2096;  // 2048 codes + 16 fp16 scales + 16 zero points
@@ -97,6 +102,18 @@ struct Format<24> {
   static constexpr int kZeroOffset = 2080;
   static constexpr int kShift = 0;
   static constexpr int kOddShift = 0;
+};
+
+// FP4: OCP MX E2M1 elements (sign, 2 exponent bits with bias 1, 1 mantissa
+// bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) in INT4's block framework.
+template <>
+struct Format<36> {
+  static constexpr bool kAsym = false;
+  static constexpr bool kFp4 = true;
+  static constexpr int kCodeBits = 4;
+  static constexpr int kTileBytes = 1152;  // 1024 + 128, as INT4
+  static constexpr int kScaleOffset = 1024;
+  static constexpr int kShift = 0;
 };
 
 // Packed codes of one 32-value block as held by its lane, by code width.
@@ -157,17 +174,27 @@ __device__ __forceinline__ float round_to_dtype(float s) {
     return (float)(__bf16)s;
 }
 
+// -0.0f in a VGPR the optimizer cannot see through: fma(x, e, -0) is exactly
+// the IEEE product x*e, but folded to a multiply it would need a separate
+// fp16 -> fp32 conversion instead of one mixed-precision FMA.
+__device__ __forceinline__ float opaque_neg_zero() {
+  float z = -0.0f;
+  asm("" : "+v"(z));
+  return z;
+}
+
 // RN32(dtype_RNE(s) * e) for two values at once: one packed conversion to the
 // dtype, then for fp16 a mixed-precision FMA that reads the fp16 halves
-// directly (fma(z, e, +0) rounds z*e once; the sign of a zero product does
-// not matter to the quantizer).
+// directly.  fma(z, e, -0) is exactly the IEEE product z*e, the sign of a zero
+// included (the FP4 codes keep it).
 template <int DT>
 __device__ __forceinline__ void round_scale2(float s0, float s1, float e, float& v0, float& v1) {
   f32x2 s = {s0, s1};
   if constexpr (DT == kFp16) {
     const f16x2 h = __builtin_convertvector(s, f16x2);
-    v0 = __builtin_fmaf((float)h.x, e, 0.0f);
-    v1 = __builtin_fmaf((float)h.y, e, 0.0f);
+    const float nz = opaque_neg_zero();
+    v0 = __builtin_fmaf((float)h.x, e, nz);
+    v1 = __builtin_fmaf((float)h.y, e, nz);
   } else {
     const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_convertvector(s, bf16x2));
     v0 = __builtin_bit_cast(float, b << 16) * e;
@@ -327,13 +354,15 @@ __device__ __forceinline__ float block_absmax(const uint32_t (&w)[kBlockValues /
 }
 
 // RN32(x * e) for the two values of a packed fp16/bf16 word (for fp16 a
-// mixed-precision FMA reads the halves directly; fma(x, e, +0) rounds x*e once).
+// mixed-precision FMA reads the halves directly; fma(x, e, -0) is exactly the
+// IEEE product x*e, the sign of a zero included).
 template <int DT>
 __device__ __forceinline__ void scale_pair(uint32_t w, float e, float& v0, float& v1) {
   if constexpr (DT == kFp16) {
     const f16x2 h = __builtin_bit_cast(f16x2, w);
-    v0 = __builtin_fmaf((float)h.x, e, 0.0f);
-    v1 = __builtin_fmaf((float)h.y, e, 0.0f);
+    const float nz = opaque_neg_zero();
+    v0 = __builtin_fmaf((float)h.x, e, nz);
+    v1 = __builtin_fmaf((float)h.y, e, nz);
   } else {
     v0 = __builtin_bit_cast(float, w << 16) * e;
     v1 = __builtin_bit_cast(float, w & 0xffff0000u) * e;
@@ -400,6 +429,81 @@ __device__ __forceinline__ void decode_block(const Block<F>& blk, float (&kk)[kB
 #pragma unroll
       for (int u = 0; u < 4; ++u) kk[8 * u + j] = sbyte(b, u);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// FP4 E2M1 block codec, with the gfx950 scaled FP4 conversions ("QuickReduce
+// INT3 quantization and benchmarking on MI355", introduction: a hardware
+// FP4 path interchangeable with INT4).  The scale operand of the conversions
+// is 1.0: the block scale is applied in fp32 beforehand (encode) or
+// afterwards (decode), so every rounding is the one the codec defines.
+// ---------------------------------------------------------------------------
+
+// Scale of a block with absolute maximum m (the maximum maps to 6):
+// d = fp16(min(m / 6, 65504)), e = fp32(1 / d) (0 if d == 0).  m * fp32(1/6)
+// differs from the correctly rounded m / 6 by at most one fp32 ulp and gives
+// the same fp16 d for every fp16 and bf16 m (checked exhaustively), so the
+// multiply stands in for the division.
+__device__ __forceinline__ uint32_t fp4_block_scale(float m, float& d, float& e) {
+  const _Float16 dh = (_Float16)__builtin_fminf(m * (1.0f / 6.0f), 65504.0f);
+  d = (float)dh;
+  e = (d == 0.0f) ? 0.0f : recip_fp16_value(d);
+  return __builtin_bit_cast(uint16_t, dh);
+}
+
+// E2M1 codes of a and b (nearest, ties to even, saturating at +-6, sign kept)
+// into byte SEL of `old`: a in the low nibble, b in the high nibble.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pack(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// E2M1 values of the low and high nibble of byte SEL of w.
+template <int SEL>
+__device__ __forceinline__ f32x2 fp4_unpack(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// Encodes one block given as 16 packed fp16/bf16 words into E2M1 unit words
+// (value j of a unit at bits 4j, as INT4).  Returns the fp16 scale bits.
+template <int DT>
+__device__ __forceinline__ uint32_t quantize_words_fp4(const uint32_t (&w)[kBlockValues / 2], CodeBlock<4>& blk) {
+  float d, e;
+  const uint32_t bits = fp4_block_scale(block_absmax<DT>(w), d, e);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) scale_pair<DT>(w[4 * u + j], e, v[2 * j], v[2 * j + 1]);
+    uint32_t r = fp4_pack<0>(0u, v[0], v[1]);
+    r = fp4_pack<1>(r, v[2], v[3]);
+    r = fp4_pack<2>(r, v[4], v[5]);
+    blk.w[u] = fp4_pack<3>(r, v[6], v[7]);
+  }
+  return bits;
+}
+
+// E2M1 unit words of 32 fp32 values v (already multiplied by the encode multiplier).
+__device__ __forceinline__ void pack_block_fp4(const float (&v)[kBlockValues], CodeBlock<4>& blk) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    uint32_t r = fp4_pack<0>(0u, v[8 * u], v[8 * u + 1]);
+    r = fp4_pack<1>(r, v[8 * u + 2], v[8 * u + 3]);
+    r = fp4_pack<2>(r, v[8 * u + 4], v[8 * u + 5]);
+    blk.w[u] = fp4_pack<3>(r, v[8 * u + 6], v[8 * u + 7]);
+  }
+}
+
+// Decodes one block into kk[i] = the E2M1 value of code i (exact; times the
+// block scale it is the decoded value, also exact).
+__device__ __forceinline__ void decode_block_fp4(const CodeBlock<4>& blk, float (&kk)[kBlockValues]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const f32x2 p0 = fp4_unpack<0>(blk.w[u]), p1 = fp4_unpack<1>(blk.w[u]);
+    const f32x2 p2 = fp4_unpack<2>(blk.w[u]), p3 = fp4_unpack<3>(blk.w[u]);
+    kk[8 * u + 0] = p0.x; kk[8 * u + 1] = p0.y; kk[8 * u + 2] = p1.x; kk[8 * u + 3] = p1.y;
+    kk[8 * u + 4] = p2.x; kk[8 * u + 5] = p2.y; kk[8 * u + 6] = p3.x; kk[8 * u + 7] = p3.y;
   }
 }
 
@@ -502,7 +606,7 @@ __device__ __forceinline__ uint32_t quantize_words_asym(const uint32_t (&w)[kBlo
 // A 32-bit constant held in a VGPR, so that a three-operand bit operation can
 // take it together with a second constant (one scalar operand per VOP3).
 __device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
-  asm volatile("" : "+v"(c));
+  asm("" : "+v"(c));
   return c;
 }
 

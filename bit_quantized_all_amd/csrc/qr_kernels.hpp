@@ -97,14 +97,18 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restr
       w[4 * j] = c.x; w[4 * j + 1] = c.y; w[4 * j + 2] = c.z; w[4 * j + 3] = c.w;
     }
     wave_lds_sync();  // the next tile overwrites this LDS tile
-    uint32_t t[kBlockValues];
     uint32_t scale;
-    if constexpr (Format<BITS>::kAsym)
-      scale = quantize_words_asym<BITS, DT>(w, t);
-    else
-      scale = quantize_words<BITS, DT>(w, t);
     Block<BITS> blk;
-    pack_block<BITS>(t, blk);
+    if constexpr (Format<BITS>::kFp4) {
+      scale = quantize_words_fp4<DT>(w, blk);
+    } else {
+      uint32_t t[kBlockValues];
+      if constexpr (Format<BITS>::kAsym)
+        scale = quantize_words_asym<BITS, DT>(w, t);
+      else
+        scale = quantize_words<BITS, DT>(w, t);
+      pack_block<BITS>(t, blk);
+    }
     store_block<BITS, QR_ENC_NT_STORE>(packed + (size_t)tile * Format<BITS>::kTileBytes, lane, blk, scale);
   }
 }
@@ -154,6 +158,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint8_t* __restr
       decode_block_asym<BITS>(blk, scale >> 16, kk);
       dd = scale_f32(scale);
       ddo = dd * (1.0f / (1 << Format<BITS>::kOddShift));
+    } else if constexpr (Format<BITS>::kFp4) {
+      decode_block_fp4(blk, kk);
+      dd = ddo = scale_f32(scale);
     } else {
       decode_block<BITS>(blk, kk);
       dd = scale_f32(scale) * (1.0f / (1 << Format<BITS>::kShift));
@@ -207,6 +214,9 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
         decode_block_asym<BI>(blk[r], sc[r] >> 16, kk);
         dd = scale_f32(sc[r]);
         ddo = dd * (1.0f / (1 << Format<BI>::kOddShift));
+      } else if constexpr (Format<BI>::kFp4) {
+        decode_block_fp4(blk[r], kk);
+        dd = ddo = scale_f32(sc[r]);
       } else {
         decode_block<BI>(blk[r], kk);
         dd = scale_f32(sc[r]) * kInvShift;
@@ -231,8 +241,8 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     // re-encode dtype_RNE(s): rounding is monotonic and symmetric, so the
     // block maximum (group range) of the rounded values is the rounded
     // maximum of |s| (range of s)
-    uint32_t t[kBlockValues];
     uint32_t scale;
+    Block<BO> ob;
     if constexpr (Format<BO>::kAsym) {
       // range ends from integer maxima of the fp32 patterns (as in quantize_words_asym)
       int hb = 0;
@@ -249,6 +259,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
       float d, e, z;
       scale = group_params<BO>(lo, hi, d, e, z);
       const float zb = z - 256.0f;
+      uint32_t t[kBlockValues];
 #pragma unroll
       for (int i = 0; i < kBlockValues; i += 2) {
         float v0, v1;
@@ -263,12 +274,31 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
         for (int i = 0; i < kBlockValues; ++i) v[i] = code_value_asym(t[i], zm) * d;
         write_lane_values<DT>(lds[wave], lane, v);
       }
+      pack_block<BO>(t, ob);
+    } else if constexpr (Format<BO>::kFp4) {
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kBlockValues; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(s[i]));
+      float d, e;
+      scale = fp4_block_scale(round_to_dtype<DT>(m), d, e);
+      float v[kBlockValues];
+#pragma unroll
+      for (int i = 0; i < kBlockValues; i += 2) round_scale2<DT>(s[i], s[i + 1], e, v[i], v[i + 1]);
+      pack_block_fp4(v, ob);
+      if constexpr (WITH_Y) {  // decode of the re-encoded sum from its codes
+        float kk[kBlockValues];
+        decode_block_fp4(ob, kk);
+#pragma unroll
+        for (int i = 0; i < kBlockValues; ++i) v[i] = kk[i] * d;
+        write_lane_values<DT>(lds[wave], lane, v);
+      }
     } else {
       float m = 0.0f;
 #pragma unroll
       for (int i = 0; i < kBlockValues; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(s[i]));
       float d, e;
       scale = block_scale<BO>(round_to_dtype<DT>(m), d, e);
+      uint32_t t[kBlockValues];
 #pragma unroll
       for (int i = 0; i < kBlockValues; i += 2) {
         float v0, v1;
@@ -282,9 +312,8 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
         for (int i = 0; i < kBlockValues; ++i) v[i] = code_value<BO>(t[i]) * d;
         write_lane_values<DT>(lds[wave], lane, v);
       }
+      pack_block<BO>(t, ob);
     }
-    Block<BO> ob;
-    pack_block<BO>(t, ob);
     store_block<BO, QR_RED_NT_STORE>(a.out + (size_t)tile * TBO, lane, ob, scale);
     if constexpr (WITH_Y) flush_tile<QR_RED_NT_STORE>(lds[wave], lane, a.y + (size_t)tile * (kTileValues * 2));
   }
@@ -366,5 +395,9 @@ qr_status launch_encode_asym(int fmt, int dt, const void* x, void* p, size_t nti
 qr_status launch_decode_asym(int fmt, int dt, const void* p, void* y, size_t ntiles, hipStream_t st);
 qr_status launch_reduce_asym_from20(int fmt_out, int dt, const ReduceArgs& a, hipStream_t st);
 qr_status launch_reduce_asym_from24(int fmt_out, int dt, const ReduceArgs& a, hipStream_t st);
+// FP4 E2M1 format (qr_fp4.hip): encode, decode and the same-format reduce.
+qr_status launch_encode_fp4(int dt, const void* x, void* p, size_t ntiles, hipStream_t st);
+qr_status launch_decode_fp4(int dt, const void* p, void* y, size_t ntiles, hipStream_t st);
+qr_status launch_reduce_fp4(int dt, const ReduceArgs& a, hipStream_t st);
 
 }  // namespace qr

@@ -13,7 +13,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqr.so")
 
 QR_OK, QR_ERR_ARG, QR_ERR_SIZE, QR_ERR_ALIGN, QR_ERR_UNSUPPORTED, QR_ERR_ALIAS, QR_ERR_HIP = range(7)
-FORMATS = {"int3": 3, "int4": 4, "int8": 8, "asym4": 20, "asym8": 24}
+FORMATS = {"int3": 3, "int4": 4, "int8": 8, "asym4": 20, "asym8": 24, "fp4": 36}
 DTYPES = {torch.float16: 0, torch.bfloat16: 1}
 TILE_VALUES = 2048
 MAX_RANKS = 16

@@ -45,6 +45,19 @@
  *          zero point above 2^b - 1 is outside the format (the encoder never
  *          writes one); decoding it gives unspecified values.
  *
+ * FP4 block format (QR_FP4; "QuickReduce INT3 quantization and benchmarking
+ * on MI355", introduction: a hardware-accelerated FP4 path on MI355 that is
+ * interchangeable with INT4; the element is OCP MX FP4 E2M1: sign, two
+ * exponent bits with bias 1, one mantissa bit, magnitudes 0, 0.5, 1, 1.5, 2,
+ * 3, 4, 6, no inf or NaN):
+ *   block  = 32 consecutive values, one fp16 scale d = fp16_RNE(min(m / 6, 65504))
+ *            (m = max|x|, so the block maximum maps to 6); e = fp32 1/d (0 if d == 0)
+ *   code   = the E2M1 value nearest to fp32(x * e), ties to an even mantissa,
+ *            magnitudes above 6 saturating to 6, the sign kept (code 8 = -0)
+ *   tile (1152 B): as INT4 -- 256 words of eight 4-bit codes (value j at bits
+ *            4j), then 64 fp16 scales at byte 1024 + 2g
+ *   decode: y = value(code) * d, exact in fp32, rounded to the I/O dtype.
+ *
  * Conventions for every call:
  *   - `n` counts values and must be a multiple of 2048 (QR_ERR_SIZE otherwise);
  *     n == 0 is a valid empty call that launches nothing and returns QR_OK.
@@ -78,9 +91,17 @@ typedef enum {
   QR_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
 } qr_status;
 
-/* Symmetric 32-value block formats are named by their code width; the
- * asymmetric 128-value group formats by 16 + code width. */
-typedef enum { QR_INT3 = 3, QR_INT4 = 4, QR_INT8 = 8, QR_ASYM4 = 20, QR_ASYM8 = 24 } qr_format;
+/* Symmetric 32-value block formats are named by their code width, the
+ * asymmetric 128-value group formats by 16 + code width, the FP4 block
+ * format by 32 + code width. */
+typedef enum {
+  QR_INT3 = 3,
+  QR_INT4 = 4,
+  QR_INT8 = 8,
+  QR_ASYM4 = 20,
+  QR_ASYM8 = 24,
+  QR_FP4 = 36
+} qr_format;
 
 typedef enum { QR_FP16 = 0, QR_BF16 = 1 } qr_dtype;
 
@@ -88,9 +109,9 @@ typedef enum { QR_FP16 = 0, QR_BF16 = 1 } qr_dtype;
 #define QR_MAX_RANKS 16
 
 /* Bytes of the packed form of n values: n / 2048 tiles of 896 (INT3), 1152
- * (INT4), 2176 (INT8), 1072 (ASYM4) or 2096 (ASYM8) bytes.  Returns 0 for an unknown format or an n that
- * is not a multiple of 2048.  Tile sizes: "Design Highlights" (INT4 1152 B,
- * INT3 896 B per 2048-value per-rank tile). */
+ * (INT4 and FP4), 2176 (INT8), 1072 (ASYM4) or 2096 (ASYM8) bytes.  Returns 0
+ * for an unknown format or an n that is not a multiple of 2048.  Tile sizes:
+ * "Design Highlights" (INT4 1152 B, INT3 896 B per 2048-value per-rank tile). */
 size_t qr_packed_bytes(qr_format fmt, size_t n);
 
 /* Send path ("Quantization and Dequantization Paths": absmax, scale, clip,
@@ -133,7 +154,7 @@ qr_status qr_reduce_compressed(qr_format fmt, qr_dtype dtype, const void *const 
  * "Flash Communication" review (fields minor_comments, section 3.2.3, and
  * forward_implications: INT4 for the reduce-scatter inputs, INT8 for the
  * all-gather payload).  Any pair of INT3/INT4/INT8 is accepted, and any pair
- * of ASYM4/ASYM8; a symmetric format paired with an asymmetric one is
+ * of ASYM4/ASYM8, and FP4 with FP4; pairs across these families are
  * QR_ERR_UNSUPPORTED.  qr_reduce_compressed(f, ...) is
  * qr_reduce_compressed_mixed(f, f, ...).
  *   packed_ranks  HOST array of R device pointers, qr_packed_bytes(fmt_in, n) each

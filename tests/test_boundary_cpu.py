@@ -40,11 +40,12 @@ def test_packed_bytes(L):
     assert L.qr_packed_bytes(20, 2048) == 1072   # ASYM4: 1024 codes + 32 scales + 16 zero points
     assert L.qr_packed_bytes(24, 2048) == 2096   # ASYM8: 2048 codes + 32 scales + 16 zero points
     assert L.qr_packed_bytes(20, 2048 * 3) == 1072 * 3
+    assert L.qr_packed_bytes(36, 2048 * 5) == 1152 * 5  # FP4: laid out as INT4
     assert L.qr_packed_bytes(4, 2048 * 65536) == 1152 * 65536
     assert L.qr_packed_bytes(4, 0) == 0
     for bad_n in (1, 2047, 2049, 4096 + 32):
         assert L.qr_packed_bytes(4, bad_n) == 0
-    for bad_fmt in (0, 2, 5, 6, 16, 19, 21, 23, 25, 28):
+    for bad_fmt in (0, 2, 5, 6, 16, 19, 21, 23, 25, 28, 32, 35, 37, 40):
         assert L.qr_packed_bytes(bad_fmt, 2048) == 0
 
 
@@ -162,3 +163,14 @@ def test_asym_validation(L):
     assert redm(L, fi=20, fo=24, out=A + 1072 - 16) == qr.QR_ERR_ALIAS
     assert redm(L, fi=24, fo=20, out=A + 2096 - 16) == qr.QR_ERR_ALIAS
     assert redm(L, fi=20, fo=20, n=0, ranks=[0], out=0, y=0) == qr.QR_OK
+
+
+def test_fp4_validation(L):
+    """FP4 passes format validation; it pairs only with itself in the mixed reduce."""
+    assert enc(L, fmt=36, n=2047) == qr.QR_ERR_SIZE
+    assert dec(L, fmt=36, p=A + 8) == qr.QR_ERR_ALIGN
+    assert red(L, fmt=36, R=0) == qr.QR_ERR_ARG
+    for fi, fo in ((4, 36), (36, 4), (36, 20), (24, 36), (36, 8)):
+        assert redm(L, fi=fi, fo=fo) == qr.QR_ERR_UNSUPPORTED, (fi, fo)
+    assert redm(L, fi=36, fo=36, out=A - 1152 + 16) == qr.QR_ERR_ALIAS
+    assert redm(L, fi=36, fo=36, n=0, ranks=[0], out=0, y=0) == qr.QR_OK

@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 FMTS = ("int3", "int4", "int8")
 AFMTS = ("asym4", "asym8")
-BITS = {"int3": 3, "int4": 4, "int8": 8, "asym4": 20, "asym8": 24}   # oracle format ids
+BITS = {"int3": 3, "int4": 4, "int8": 8, "asym4": 20, "asym8": 24, "fp4": 36}   # oracle format ids
 DT = {"fp16": torch.float16, "bf16": torch.bfloat16}
 
 
@@ -291,6 +291,25 @@ def test_block_scale_every_fp16_scale():
     assert counters.cpu().tolist() == [0] * 6
 
 
+def test_fp4_hardware_conversions_and_scale():
+    """The FP4 device functions against definitions in the test helper: the
+    gfx950 scaled FP4 conversion (scale 1.0) on every non-NaN fp32 pattern is
+    the nearest E2M1 value with ties to an even mantissa, saturating at 6,
+    sign kept, nibbles and byte position as the tile layout needs; the
+    reverse conversion gives the E2M1 values for every byte and position; the
+    FP4 block scale and multiplier are right for every fp16 and bf16 maximum."""
+    import ctypes
+    import os
+    lib = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gpu_helpers", "libscale_check.so")
+    L = ctypes.CDLL(lib)
+    L.qr_test_fp4_check.argtypes = [ctypes.c_void_p]
+    counters = torch.tensor([0, -1, 0, 0, 0], dtype=torch.int32, device="cuda")
+    log("fp4 conversions: every fp32 pattern, every byte, every fp16/bf16 block maximum")
+    assert L.qr_test_fp4_check(counters.data_ptr()) == 0
+    c = counters.cpu().tolist()
+    assert c == [0, -1, 0, 0, 0], f"mismatches {c[0]} (first pattern {c[1] & 0xFFFFFFFF:#010x}), unpack {c[2]}, scale fp16 {c[3]} bf16 {c[4]}"
+
+
 MIXED = [("int4", "int8"), ("int3", "int4"), ("int3", "int8"), ("int4", "int3"), ("int8", "int3"),
          ("int8", "int4")]
 
@@ -492,3 +511,96 @@ def test_asym_hand_built_groups(qa, oracle):
             codes, sb, zp = P.asym_unpack(bits, got)
             assert sb[0, 0] == want_sb and zp[0, 0] == qmax, (fmt, dtype)
             assert np.array_equal(got, oracle.encode(BITS[fmt], dtype, xb)), (fmt, dtype)
+
+
+# ---------------------------------------------------------------------------
+# FP4 E2M1 block codec (hardware conversions)
+# ---------------------------------------------------------------------------
+
+def gen_fp4(kind, dtype, n, seed):
+    """Value families for FP4: the common ones, plus blocks on the E2M1 grid
+    (v * s with a 6 * s anchor) and blocks of midpoints between E2M1 values
+    (ties at every spacing)."""
+    if kind not in ("grid", "ties"):
+        return gen(kind, dtype, n, seed)
+    rng = np.random.default_rng(seed)
+    nb = n // 32
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    if kind == "grid":
+        v = mags[rng.integers(0, 8, size=(nb, 32))]
+    else:
+        mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+        v = mids[rng.integers(0, 7, size=(nb, 32))]
+    v = v * np.where(rng.random((nb, 32)) < 0.5, -1.0, 1.0)
+    v[:, 0] = 6.0
+    x = (v * 2.0 ** rng.integers(-12, 8, size=(nb, 1))).ravel()
+    if dtype == "fp16":
+        return P.f16_bits(np.clip(x, -65504, 65504))
+    return P.bf16_bits(x.astype(np.float32).astype(np.float64))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("ntiles", [1, 5, 37, 1031])
+@pytest.mark.parametrize("kind", ["normal", "outliers", "scales", "specials", "grid", "ties"])
+def test_fp4_encode_decode_parity(qa, oracle, dtype, ntiles, kind):
+    n = ntiles * 2048
+    xb = gen_fp4(kind, dtype, n, seed=ntiles * 17 + len(kind))
+    log(f"fp4 encode/decode {dtype} tiles={ntiles} {kind}")
+    p = qa.qr_encode("fp4", dev(xb, DT[dtype]))
+    y = qa.qr_decode("fp4", p, n, DT[dtype])
+    torch.cuda.synchronize()
+    want_p = oracle.encode(36, dtype, xb)
+    got_p = p.cpu().numpy()
+    assert np.array_equal(got_p, want_p), f"packed bytes differ at {first_diff(got_p, want_p)}"
+    assert np.array_equal(u16(y), oracle.decode(36, dtype, want_p, n))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_fp4_decode_arbitrary_packed(qa, oracle, dtype):
+    """Every code with every finite fp16 scale class (zero, subnormal, largest)."""
+    rng = np.random.default_rng(36)
+    T = 517
+    codes = rng.integers(0, 16, size=(T, 2048))
+    sb = rng.integers(0, 0x7C00, size=(T, 64)).astype(np.uint16)
+    sb[:, :3] = [0, 1, 0x7BFF]
+    packed = P.pack(4, codes, sb)
+    log(f"fp4 decode arbitrary {dtype}")
+    y = qa.qr_decode("fp4", dev(packed), T * 2048, DT[dtype])
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(y), oracle.decode(36, dtype, packed, T * 2048))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 16])
+@pytest.mark.parametrize("ntiles", [3, 133])
+def test_fp4_reduce_parity(qa, oracle, dtype, R, ntiles):
+    n = ntiles * 2048
+    kinds = ["normal", "grid", "scales", "ties", "outliers", "specials"]
+    xs = [gen_fp4(kinds[r % 6], dtype, n, seed=3000 * R + 10 * r + ntiles) for r in range(R)]
+    log(f"fp4 reduce {dtype} R={R} tiles={ntiles}")
+    packed = [qa.qr_encode("fp4", dev(x, DT[dtype])) for x in xs]
+    out, y = qa.qr_reduce_compressed("fp4", DT[dtype], packed, n)
+    out2, none = qa.qr_reduce_compressed("fp4", DT[dtype], packed, n, with_output=False)
+    torch.cuda.synchronize()
+    assert none is None
+    wranks = [oracle.encode(36, dtype, x) for x in xs]
+    for r in range(R):
+        assert np.array_equal(packed[r].cpu().numpy(), wranks[r]), r
+    wout, wy = oracle.reduce(36, dtype, wranks, n)
+    got = out.cpu().numpy()
+    assert np.array_equal(got, wout), f"re-encoded tiles differ at {first_diff(got, wout)}"
+    assert np.array_equal(u16(y), wy)
+    assert np.array_equal(out2.cpu().numpy(), wout)
+
+
+def test_fp4_reduce_fp16_overflow(qa, oracle):
+    """fp16 sums that overflow to +-inf: scale saturates at 65504, codes +-6."""
+    n = 2 * 2048
+    xb = [P.f16_bits(np.full(n, 60000.0)) for r in range(3)]
+    xb[1][::3] = P.f16_bits(-60000.0)
+    log("fp4 reduce fp16 overflow")
+    packed = [qa.qr_encode("fp4", dev(x, torch.float16)) for x in xb]
+    out, y = qa.qr_reduce_compressed("fp4", torch.float16, packed, n)
+    torch.cuda.synchronize()
+    wout, wy = oracle.reduce(36, "fp16", [oracle.encode(36, "fp16", x) for x in xb], n)
+    assert np.array_equal(out.cpu().numpy(), wout) and np.array_equal(u16(y), wy)

@@ -25,6 +25,7 @@ tiles):
                            group codec (128-value groups, scale + zero point).
   asym6_r8_fp16_32x1024x4096  the same inputs, asymmetric 4-bit reduce inputs
                            and an asymmetric 8-bit re-encoded sum.
+  fp4_r8_fp16_32x1024x4096  the same inputs through the FP4 E2M1 block codec.
 
 Random numbers come from torch's seeded generators (Philox on the GPU, the CPU
 generator on the host); each (seed, workload, rank) gets its own stream seed.
@@ -40,7 +41,7 @@ MIB = 1 << 20
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    fmt: str                 # "int3" | "int4" | "int8" | "asym4" | "asym8"
+    fmt: str                 # "int3" | "int4" | "int8" | "asym4" | "asym8" | "fp4"
     dtype: torch.dtype       # torch.float16 | torch.bfloat16
     ranks: int               # R simulated rank buffers (1 = encode/decode only)
     n: int                   # values per rank
@@ -96,6 +97,11 @@ WORKLOADS = {
                                            32 * 1024 * 4096, (32, 1024, 4096),
                                            channel_sigma=(0.01, 20.0), fmt_out="asym8",
                                            data_key="int4_r8_fp16_32x1024x4096"),
+    # FP4 E2M1 block codec on the same activations
+    "fp4_r8_fp16_32x1024x4096": Workload("fp4_r8_fp16_32x1024x4096", "fp4", torch.float16, 8,
+                                         32 * 1024 * 4096, (32, 1024, 4096),
+                                         channel_sigma=(0.01, 20.0),
+                                         data_key="int4_r8_fp16_32x1024x4096"),
 }
 
 BENCH_WORKLOAD = "int4_r8_fp16_32x1024x4096"
