@@ -11,9 +11,11 @@ The reported value is GB/s of FP16 input: R * n * 2 bytes per step divided by
 the step time.  Alongside: the pipeline's algorithmic HBM bytes as % of the
 MI355X peak (8 TB/s), the dominant kernel's roofline (average launch duration
 from HIP events on the launch stream), and the CPU oracle timed on a bounded
-sample of the same input.
+sample of the same input.  With --graph the timed launches are captured in
+HIP graphs and replayed, which removes the host-side cost of issuing each
+launch from Python (it bounds steps on small messages).
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--graph]
 """
 import argparse
 import hashlib
@@ -170,6 +172,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the timed launches in HIP graphs and replay them (removes the "
+                         "host-side launch cost that bounds small messages)")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also time a plain device copy of one rank's input (bandwidth reference and "
                          "calibration kernel for the HBM traffic counters)")
@@ -206,23 +211,37 @@ def main():
     y = torch.empty(w.n, dtype=w.dtype, device=dev)
     torch.cuda.synchronize()
 
+    # Every launch goes to the current stream: the timing stream when eager, the
+    # capture stream while a graph is being recorded.
     def encode(r):
-        qa.qr_encode(w.fmt, xs[r], packed[r], stream=stream)
+        qa.qr_encode(w.fmt, xs[r], packed[r])
 
     def finish():
         if w.reduce:
-            qa.qr_reduce_compressed_mixed(w.fmt, w.out_fmt, w.dtype, packed, w.n, packed_out=out, y_out=y,
-                                          stream=stream)
+            qa.qr_reduce_compressed_mixed(w.fmt, w.out_fmt, w.dtype, packed, w.n, packed_out=out, y_out=y)
         else:
-            qa.qr_decode(w.fmt, packed[0], w.n, w.dtype, y=y, stream=stream)
+            qa.qr_decode(w.fmt, packed[0], w.n, w.dtype, y=y)
 
     def step():
         for r in range(w.ranks):
             encode(r)
         finish()
 
+    def runner(fn):
+        """fn itself (eager), or a function that replays fn captured in a HIP graph."""
+        if not args.graph:
+            return fn
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g.replay
+
     for _ in range(args.warmup):
         step()
+    torch.cuda.synchronize()
+    run_step = runner(step)
+    run_step()
     torch.cuda.synchronize()
 
     # timed region 1: K clean steps between two events
@@ -230,7 +249,7 @@ def main():
     torch.cuda.synchronize()
     start.record(stream)
     for _ in range(args.steps):
-        step()
+        run_step()
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
@@ -238,10 +257,11 @@ def main():
     # timed region 2: each kernel alone, K steps' worth of back-to-back launches
     # between two events on the launch stream -> average launch duration
     def timed(fn, launches):
+        run = runner(fn)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
-        fn()
+        run()
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / launches * 1e3
@@ -252,6 +272,8 @@ def main():
                         args.steps * w.ranks),
         kname: timed(lambda: [finish() for _ in range(args.steps)], args.steps),
     }
+    run_step()   # the outputs checked below come from one whole step
+    torch.cuda.synchronize()
     print(f"# {name}: {ms_per_step:.4f} ms/step; per-launch us: "
           + ", ".join(f"{k}={v:.2f}" for k, v in kern_us.items()), file=sys.stderr, flush=True)
 
@@ -312,6 +334,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
+        "launch": "hip_graph" if args.graph else "eager",
         "config": {"workload": name, "format": w.fmt, "format_out": w.out_fmt, "io_dtype": w.io_dtype,
                    "ranks": w.ranks,
                    "values_per_rank": w.n, "shape": list(w.shape), "seed": args.seed},

@@ -604,3 +604,40 @@ def test_fp4_reduce_fp16_overflow(qa, oracle):
     torch.cuda.synchronize()
     wout, wy = oracle.reduce(36, "fp16", [oracle.encode(36, "fp16", x) for x in xb], n)
     assert np.array_equal(out.cpu().numpy(), wout) and np.array_equal(u16(y), wy)
+
+
+def test_graph_replay_matches_eager(qa):
+    """A step (R encodes + the fused reduce) captured in a HIP graph and
+    replayed three times, with eager work and synchronizations in between:
+    every replay rewrites the outputs (cleared with an eager fill before it)
+    with exactly the bytes of the eager step."""
+    w = W.small(W.WORKLOADS["int4_r8_fp16_32x1024x4096"], 16 * 2048 * 4)
+    xs = [x.cuda() for x in W.inputs(w, seed=5)]
+    packed = [torch.empty(qa.qr_packed_bytes("int4", w.n), dtype=torch.uint8, device="cuda") for _ in xs]
+    out = torch.empty(qa.qr_packed_bytes("int4", w.n), dtype=torch.uint8, device="cuda")
+    y = torch.empty(w.n, dtype=w.dtype, device="cuda")
+
+    def step():
+        for x, p in zip(xs, packed):
+            qa.qr_encode("int4", x, p)
+        qa.qr_reduce_compressed("int4", w.dtype, packed, w.n, packed_out=out, y_out=y)
+
+    log("graph replay vs eager")
+    step()
+    torch.cuda.synchronize()
+    want = [p.clone() for p in packed] + [out.clone(), y.view(torch.int16).clone()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in packed + [out]:
+            t.fill_(0xA5)
+        y.fill_(-1.0)
+        other = qa.qr_encode("int8", xs[rep])   # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [p.clone() for p in packed] + [out.clone(), y.view(torch.int16).clone()]
+        assert all(torch.equal(a, b) for a, b in zip(got, want)), rep
+        del other
