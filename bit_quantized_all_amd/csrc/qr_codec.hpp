@@ -675,6 +675,47 @@ __device__ __forceinline__ void st(T v, T* p) {
     *p = v;
 }
 
+// ---------------------------------------------------------------------------
+// 8-bit codes (INT8, ASYM8): a lane's block is 32 contiguous bytes, so loading
+// or storing it directly would make every 16-byte access of the wave stride by
+// 32 bytes.  Instead the wave moves row-order 16-byte chunks (lane l: chunks
+// l and 64 + l, coalesced) and exchanges them through a wave-private 2 KB LDS
+// region (lane l: chunks 2l and 2l + 1).  Chunk c sits in slot
+// c ^ ((c >> 1) & 15), which keeps both access orders free of bank conflicts
+// within every 8 and every 16 consecutive lanes.
+// ---------------------------------------------------------------------------
+
+template <int F>
+constexpr bool kStaged = Format<F>::kCodeBits == 8;
+
+__device__ __forceinline__ int swz8(int c) { return c ^ ((c >> 1) & 15); }
+
+// Row-order chunks (held in blk.w[0..3] = chunk l, blk.w[4..7] = chunk 64 + l)
+// to the lane's own block (its 32 code bytes in order).  tl: 128 chunks.
+__device__ __forceinline__ void stage_codes_in(u32x4* tl, int lane, CodeBlock<8>& blk) {
+  tl[swz8(lane)] = u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]};
+  tl[swz8(64 + lane)] = u32x4{blk.w[4], blk.w[5], blk.w[6], blk.w[7]};
+  wave_lds_sync();
+  const u32x4 a = tl[swz8(2 * lane)], b = tl[swz8(2 * lane + 1)];
+  wave_lds_sync();
+  blk.w[0] = a.x; blk.w[1] = a.y; blk.w[2] = a.z; blk.w[3] = a.w;
+  blk.w[4] = b.x; blk.w[5] = b.y; blk.w[6] = b.z; blk.w[7] = b.w;
+}
+
+// The lane's block to row-order chunks, stored coalesced at tile + 16 * lane
+// and tile + 1024 + 16 * lane.
+template <bool NT>
+__device__ __forceinline__ void stage_codes_out(u32x4* tl, int lane, const CodeBlock<8>& blk,
+                                                uint8_t* __restrict__ tile) {
+  tl[swz8(2 * lane)] = u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]};
+  tl[swz8(2 * lane + 1)] = u32x4{blk.w[4], blk.w[5], blk.w[6], blk.w[7]};
+  wave_lds_sync();
+  const u32x4 a = tl[swz8(lane)], b = tl[swz8(64 + lane)];
+  wave_lds_sync();
+  st<NT>(a, reinterpret_cast<u32x4*>(tile) + lane);
+  st<NT>(b, reinterpret_cast<u32x4*>(tile) + 64 + lane);
+}
+
 // Codes of block g and its scale.  For the asymmetric formats `scale`
 // receives one dword of the tile's 48-byte scale / zero-point region (dword
 // min(g & 15, 11)), and group_meta() later hands every lane its group's
@@ -687,8 +728,9 @@ __device__ __forceinline__ void load_block(const uint8_t* __restrict__ tile, int
     const u32x4 v = ld<NT>(reinterpret_cast<const u32x4*>(tile + 16 * g));
     blk.w[0] = v.x; blk.w[1] = v.y; blk.w[2] = v.z; blk.w[3] = v.w;
   } else if constexpr (BITS == 8) {
-    const u32x4 a = ld<NT>(reinterpret_cast<const u32x4*>(tile + 32 * g));
-    const u32x4 b = ld<NT>(reinterpret_cast<const u32x4*>(tile + 32 * g + 16));
+    // row-order chunks g and 64 + g; stage_codes_in() turns them into block g
+    const u32x4 a = ld<NT>(reinterpret_cast<const u32x4*>(tile) + g);
+    const u32x4 b = ld<NT>(reinterpret_cast<const u32x4*>(tile) + 64 + g);
     blk.w[0] = a.x; blk.w[1] = a.y; blk.w[2] = a.z; blk.w[3] = a.w;
     blk.w[4] = b.x; blk.w[5] = b.y; blk.w[6] = b.z; blk.w[7] = b.w;
   } else {
@@ -718,6 +760,7 @@ __device__ __forceinline__ uint32_t group_meta(uint32_t m, int g) {
 
 // Stores block g; for the asymmetric formats the first lane of each group
 // stores the group's scale and zero point (scale bits | zero point << 16).
+// 8-bit codes are stored by stage_codes_out(), only their scale here.
 template <int F, bool NT>
 __device__ __forceinline__ void store_block(uint8_t* __restrict__ tile, int g, const Block<F>& blk,
                                             uint32_t scale) {
@@ -725,8 +768,7 @@ __device__ __forceinline__ void store_block(uint8_t* __restrict__ tile, int g, c
   if constexpr (BITS == 4) {
     st<NT>(u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]}, reinterpret_cast<u32x4*>(tile + 16 * g));
   } else if constexpr (BITS == 8) {
-    st<NT>(u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]}, reinterpret_cast<u32x4*>(tile + 32 * g));
-    st<NT>(u32x4{blk.w[4], blk.w[5], blk.w[6], blk.w[7]}, reinterpret_cast<u32x4*>(tile + 32 * g + 16));
+    // the codes go through stage_codes_out(); only the scale is stored here
   } else {
     st<NT>(u32x2{blk.low[0], blk.low[1]}, reinterpret_cast<u32x2*>(tile + 8 * g));
     st<NT>(blk.high, reinterpret_cast<uint32_t*>(tile + Format<3>::kHighOffset + 4 * g));

@@ -109,7 +109,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restr
         scale = quantize_words<BITS, DT>(w, t);
       pack_block<BITS>(t, blk);
     }
-    store_block<BITS, QR_ENC_NT_STORE>(packed + (size_t)tile * Format<BITS>::kTileBytes, lane, blk, scale);
+    uint8_t* tp = packed + (size_t)tile * Format<BITS>::kTileBytes;
+    if constexpr (kStaged<BITS>) stage_codes_out<QR_ENC_NT_STORE>(tl, lane, blk, tp);
+    store_block<BITS, QR_ENC_NT_STORE>(tp, lane, blk, scale);
   }
 }
 
@@ -151,6 +153,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint8_t* __restr
     Block<BITS> blk;
     uint32_t scale;
     load_block<BITS, QR_DEC_NT_LOAD>(packed + (size_t)tile * Format<BITS>::kTileBytes, lane, blk, scale);
+    if constexpr (kStaged<BITS>) stage_codes_in(lds[wave], lane, blk);
     float kk[kBlockValues];
     float dd, ddo;  // scales of even and odd values
     if constexpr (Format<BITS>::kAsym) {
@@ -188,7 +191,10 @@ struct ReduceArgs {
 
 template <int BI, int BO, int DT, int R, bool WITH_Y>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
-  __shared__ u32x4 lds[WITH_Y ? kWavesPerGroup : 1][WITH_Y ? kChunks : 1];
+  // per wave: the fp16/bf16 output tile (WITH_Y) and / or the 2 KB staging
+  // region of 8-bit codes, which reuses the output tile's space
+  constexpr int kLdsChunks = WITH_Y ? kChunks : ((kStaged<BI> || kStaged<BO>) ? kChunks / 2 : 1);
+  __shared__ u32x4 lds[kWavesPerGroup][kLdsChunks];
   constexpr int TB = Format<BI>::kTileBytes;    // input tiles
   constexpr int TBO = Format<BO>::kTileBytes;   // re-encoded tiles
   constexpr float kInvShift = 1.0f / (1 << Format<BI>::kShift);
@@ -207,6 +213,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     float s[kBlockValues];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
+      if constexpr (kStaged<BI>) stage_codes_in(lds[wave], lane, blk[r]);
       float kk[kBlockValues];
       float dd, ddo;  // scales of even and odd values (exact products with kk)
       if constexpr (Format<BI>::kAsym) {
@@ -243,6 +250,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     // maximum of |s| (range of s)
     uint32_t scale;
     Block<BO> ob;
+    float yv[kBlockValues];  // decoded re-encoded sum (WITH_Y)
     if constexpr (Format<BO>::kAsym) {
       // range ends from integer maxima of the fp32 patterns (as in quantize_words_asym)
       int hb = 0;
@@ -269,10 +277,8 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
       }
       if constexpr (WITH_Y) {  // decode of the re-encoded sum, straight from the codes
         const float zm = 8388608.0f + z;
-        float v[kBlockValues];
 #pragma unroll
-        for (int i = 0; i < kBlockValues; ++i) v[i] = code_value_asym(t[i], zm) * d;
-        write_lane_values<DT>(lds[wave], lane, v);
+        for (int i = 0; i < kBlockValues; ++i) yv[i] = code_value_asym(t[i], zm) * d;
       }
       pack_block<BO>(t, ob);
     } else if constexpr (Format<BO>::kFp4) {
@@ -289,8 +295,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
         float kk[kBlockValues];
         decode_block_fp4(ob, kk);
 #pragma unroll
-        for (int i = 0; i < kBlockValues; ++i) v[i] = kk[i] * d;
-        write_lane_values<DT>(lds[wave], lane, v);
+        for (int i = 0; i < kBlockValues; ++i) yv[i] = kk[i] * d;
       }
     } else {
       float m = 0.0f;
@@ -307,14 +312,21 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
         t[i + 1] = quantize<BO>(v1);
       }
       if constexpr (WITH_Y) {  // decode of the re-encoded sum, straight from the codes
-        float v[kBlockValues];
 #pragma unroll
-        for (int i = 0; i < kBlockValues; ++i) v[i] = code_value<BO>(t[i]) * d;
-        write_lane_values<DT>(lds[wave], lane, v);
+        for (int i = 0; i < kBlockValues; ++i) yv[i] = code_value<BO>(t[i]) * d;
       }
       pack_block<BO>(t, ob);
     }
-    store_block<BO, QR_RED_NT_STORE>(a.out + (size_t)tile * TBO, lane, ob, scale);
+    uint8_t* otile = a.out + (size_t)tile * TBO;
+    if constexpr (kStaged<BO>) {
+      // codes through the LDS staging region first, then the output tile
+      stage_codes_out<QR_RED_NT_STORE>(lds[wave], lane, ob, otile);
+      store_block<BO, QR_RED_NT_STORE>(otile, lane, ob, scale);
+      if constexpr (WITH_Y) write_lane_values<DT>(lds[wave], lane, yv);
+    } else {
+      if constexpr (WITH_Y) write_lane_values<DT>(lds[wave], lane, yv);
+      store_block<BO, QR_RED_NT_STORE>(otile, lane, ob, scale);
+    }
     if constexpr (WITH_Y) flush_tile<QR_RED_NT_STORE>(lds[wave], lane, a.y + (size_t)tile * (kTileValues * 2));
   }
 }
