@@ -65,8 +65,15 @@ TEST_HELPER_SRCS = [os.path.join(ROOT, "tests", "gpu_helpers", f) for f in ("sca
 TEST_HELPER_LIB = os.path.join(ROOT, "tests", "gpu_helpers", "libscale_check.so")
 
 
+SMALL_GRID_LIB = os.path.join(ROOT, "tests", "gpu_helpers", "libqr_smallgrid.so")
+
+
 def build_test_helpers(quiet=True):
-    """Test-only HIP helper that exercises the codec's device functions directly."""
+    """Test-only HIP libraries: a helper that exercises the codec's device
+    functions directly, and the library itself built with its grid capped at 3
+    workgroups, so that every kernel's grid-stride loop (and the encode's
+    prefetch of the next tile) runs at small sizes."""
+    build(out=SMALL_GRID_LIB, extra=["-DQR_MAX_GROUPS=3"], quiet=quiet)
     return build(out=TEST_HELPER_LIB, sources=TEST_HELPER_SRCS, quiet=quiet)
 
 

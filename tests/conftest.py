@@ -14,7 +14,7 @@ def pytest_configure(config):
     from bit_quantized_all_amd import build as hip_build
     if not os.path.exists(hip_build.LIB):
         hip_build.build()
-    if not os.path.exists(hip_build.TEST_HELPER_LIB):
+    if not (os.path.exists(hip_build.TEST_HELPER_LIB) and os.path.exists(hip_build.SMALL_GRID_LIB)):
         hip_build.build_test_helpers()
 
 

@@ -641,3 +641,61 @@ def test_graph_replay_matches_eager(qa):
         got = [p.clone() for p in packed] + [out.clone(), y.view(torch.int16).clone()]
         assert all(torch.equal(a, b) for a, b in zip(got, want)), rep
         del other
+
+
+# ---------------------------------------------------------------------------
+# grid-stride loops: the library built with its grid capped at 3 workgroups
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def small_grid():
+    import ctypes
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gpu_helpers", "libqr_smallgrid.so")
+    L = ctypes.CDLL(path)
+    vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    L.qr_packed_bytes.restype = sz
+    L.qr_packed_bytes.argtypes = [i, sz]
+    L.qr_encode.argtypes = [i, i, vp, vp, sz, vp]
+    L.qr_decode.argtypes = [i, i, vp, vp, sz, vp]
+    L.qr_reduce_compressed.argtypes = [i, i, ctypes.POINTER(vp), i, vp, vp, sz, vp]
+    return L
+
+
+@pytest.mark.parametrize("fmt", ["int3", "int4", "int8", "asym4", "asym8", "fp4"])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_grid_stride_loops(small_grid, oracle, fmt, dtype):
+    """With 3 workgroups (12 waves) every wave loops over many tiles, and the
+    encode prefetches each next tile while it encodes the current one: encode,
+    decode and the reduce (R = 3, with and without y) against the oracle, on
+    a tile count that the 12 waves do not divide."""
+    import ctypes
+    L = small_grid
+    fid, dt = BITS[fmt], (0 if dtype == "fp16" else 1)
+    ntiles = 151
+    n = ntiles * 2048
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    kinds = ["normal", "scales", "specials"]
+    xs = [gen(kinds[r], dtype, n, seed=500 + 10 * r + fid) for r in range(3)]
+    log(f"grid-stride loops {fmt} {dtype} tiles={ntiles}")
+    pb = L.qr_packed_bytes(fid, n)
+    xd = [dev(x, DT[dtype]) for x in xs]
+    packed = [torch.empty(pb, dtype=torch.uint8, device="cuda") for _ in xs]
+    for x, p in zip(xd, packed):
+        assert L.qr_encode(fid, dt, x.data_ptr(), p.data_ptr(), n, st) == 0
+    y = torch.empty(n, dtype=DT[dtype], device="cuda")
+    assert L.qr_decode(fid, dt, packed[0].data_ptr(), y.data_ptr(), n, st) == 0
+    out = torch.empty(pb, dtype=torch.uint8, device="cuda")
+    out2 = torch.empty(pb, dtype=torch.uint8, device="cuda")
+    yr = torch.empty(n, dtype=DT[dtype], device="cuda")
+    arr = (ctypes.c_void_p * 3)(*[p.data_ptr() for p in packed])
+    assert L.qr_reduce_compressed(fid, dt, arr, 3, out.data_ptr(), yr.data_ptr(), n, st) == 0
+    assert L.qr_reduce_compressed(fid, dt, arr, 3, out2.data_ptr(), None, n, st) == 0
+    torch.cuda.synchronize()
+    wr = [oracle.encode(fid, dtype, x) for x in xs]
+    for r in range(3):
+        assert np.array_equal(packed[r].cpu().numpy(), wr[r]), r
+    assert np.array_equal(u16(y), oracle.decode(fid, dtype, wr[0], n))
+    wout, wy = oracle.reduce(fid, dtype, wr, n)
+    assert np.array_equal(out.cpu().numpy(), wout) and np.array_equal(out2.cpu().numpy(), wout)
+    assert np.array_equal(u16(yr), wy)
