@@ -160,7 +160,14 @@ def cpu_baseline(w, xs, out, y, seconds):
     sample = (f"first {done} tiles ({done * 2048} values) of each of the {w.ranks} rank buffers of "
               f"{w.name}: oracle encode x{w.ranks} + " + ("reduce with decode" if w.reduce else "decode")
               + f", {busy:.1f} s of oracle time, one thread")
-    return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": sample}, ok
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": sample,
+            "cpu_model": model, "host_cpus": os.cpu_count()}, ok
 
 
 def main():
@@ -172,6 +179,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate-mib", type=int, default=512,
+                    help="rotate through enough identical buffer sets (inputs, packed, outputs) that "
+                         "one pass over them touches at least this many MiB, so that the 256 MB "
+                         "last-level cache cannot hold the working set (at most 64 sets)")
     ap.add_argument("--graph", action="store_true",
                     help="capture the timed launches in HIP graphs and replay them (removes the "
                          "host-side launch cost that bounds small messages)")
@@ -204,28 +215,37 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
 
-    xs = W.inputs(w, seed=args.seed, device=dev)
     pb = qa.qr_packed_bytes(w.fmt, w.n)
-    packed = [torch.empty(pb, dtype=torch.uint8, device=dev) for _ in range(w.ranks)]
-    out = torch.empty(qa.qr_packed_bytes(w.out_fmt, w.n), dtype=torch.uint8, device=dev) if w.reduce else None
-    y = torch.empty(w.n, dtype=w.dtype, device=dev)
+    pbo = qa.qr_packed_bytes(w.out_fmt, w.n)
+    set_bytes = w.ranks * (2 * w.n + pb) + (pbo if w.reduce else 0) + 2 * w.n
+    nsets = max(1, min(64, -(-(args.rotate_mib << 20) // set_bytes)))
+
+    class BufferSet:
+        def __init__(self, xs):
+            self.xs = xs
+            self.packed = [torch.empty(pb, dtype=torch.uint8, device=dev) for _ in range(w.ranks)]
+            self.out = torch.empty(pbo, dtype=torch.uint8, device=dev) if w.reduce else None
+            self.y = torch.empty(w.n, dtype=w.dtype, device=dev)
+
+    xs = W.inputs(w, seed=args.seed, device=dev)
+    sets = [BufferSet(xs)] + [BufferSet([x.clone() for x in xs]) for _ in range(nsets - 1)]
     torch.cuda.synchronize()
 
     # Every launch goes to the current stream: the timing stream when eager, the
     # capture stream while a graph is being recorded.
-    def encode(r):
-        qa.qr_encode(w.fmt, xs[r], packed[r])
+    def encode(b, r):
+        qa.qr_encode(w.fmt, b.xs[r], b.packed[r])
 
-    def finish():
+    def finish(b):
         if w.reduce:
-            qa.qr_reduce_compressed_mixed(w.fmt, w.out_fmt, w.dtype, packed, w.n, packed_out=out, y_out=y)
+            qa.qr_reduce_compressed_mixed(w.fmt, w.out_fmt, w.dtype, b.packed, w.n, packed_out=b.out, y_out=b.y)
         else:
-            qa.qr_decode(w.fmt, packed[0], w.n, w.dtype, y=y)
+            qa.qr_decode(w.fmt, b.packed[0], w.n, w.dtype, y=b.y)
 
-    def step():
+    def step(b):
         for r in range(w.ranks):
-            encode(r)
-        finish()
+            encode(b, r)
+        finish(b)
 
     def runner(fn):
         """fn itself (eager), or a function that replays fn captured in a HIP graph."""
@@ -237,19 +257,20 @@ def main():
         torch.cuda.synchronize()
         return g.replay
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(max(args.warmup, nsets)):
+        step(sets[i % nsets])
     torch.cuda.synchronize()
-    run_step = runner(step)
-    run_step()
+    run_steps = [runner(lambda b=b: step(b)) for b in sets]
+    for run in run_steps:
+        run()
     torch.cuda.synchronize()
 
-    # timed region 1: K clean steps between two events
+    # timed region 1: K clean steps between two events, rotating the buffer sets
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for _ in range(args.steps):
-        run_step()
+    for i in range(args.steps):
+        run_steps[i % nsets]()
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
@@ -268,12 +289,13 @@ def main():
 
     kname = "reduce" if w.reduce else "decode"
     kern_us = {
-        "encode": timed(lambda: [encode(r) for _ in range(args.steps) for r in range(w.ranks)],
+        "encode": timed(lambda: [encode(sets[i % nsets], r) for i in range(args.steps) for r in range(w.ranks)],
                         args.steps * w.ranks),
-        kname: timed(lambda: [finish() for _ in range(args.steps)], args.steps),
+        kname: timed(lambda: [finish(sets[i % nsets]) for i in range(args.steps)], args.steps),
     }
-    run_step()   # the outputs checked below come from one whole step
+    run_steps[0]()   # the outputs checked below come from one whole step on set 0
     torch.cuda.synchronize()
+    packed, out, y = sets[0].packed, sets[0].out, sets[0].y
     print(f"# {name}: {ms_per_step:.4f} ms/step; per-launch us: "
           + ", ".join(f"{k}={v:.2f}" for k, v in kern_us.items()), file=sys.stderr, flush=True)
 
@@ -337,7 +359,8 @@ def main():
         "launch": "hip_graph" if args.graph else "eager",
         "config": {"workload": name, "format": w.fmt, "format_out": w.out_fmt, "io_dtype": w.io_dtype,
                    "ranks": w.ranks,
-                   "values_per_rank": w.n, "shape": list(w.shape), "seed": args.seed},
+                   "values_per_rank": w.n, "shape": list(w.shape), "seed": args.seed,
+                   "buffer_sets": nsets, "set_mib": round(set_bytes / 2 ** 20, 1)},
         "pct_hbm_peak": round(100 * pipe_gbs / PEAK_HBM_GBS, 2),
         "pipeline_hbm_gbs": round(pipe_gbs, 1),
         "roofline": roofline,

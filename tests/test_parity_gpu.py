@@ -234,22 +234,27 @@ def check_tiles(oracle, w, xs_host_tiles, packed, out, y, tiles):
     assert np.array_equal(y[idx_v], wy), "decoded sum differs"
 
 
-def test_smallest_workload_exact(qa, oracle):
-    """configs[0]-sized workload, every value."""
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_smallest_workload_exact(qa, oracle, seed):
+    """The INT3 R=2 8192-value workload, every value, seeds 0..2."""
     w = W.WORKLOADS["int3_r2_fp16_8k"]
-    xs = W.inputs(w, seed=0)
-    log("workload int3_r2_fp16_8k")
+    xs = W.inputs(w, seed=seed)
+    log(f"workload int3_r2_fp16_8k seed={seed}")
     packed, out, y = run_pipeline(qa, w, [x.cuda() for x in xs])
     torch.cuda.synchronize()
     check_tiles(oracle, w, [u16(x) for x in xs], [p.cpu().numpy() for p in packed],
                 out.cpu().numpy(), u16(y), list(range(w.n // 2048)))
 
 
-@pytest.mark.parametrize("name", [k for k in W.WORKLOADS if k != "int3_r2_fp16_8k"])
-def test_workload_full_size_sampled(qa, oracle, name):
+FULL_SIZE_CASES = [(k, seed) for k in W.WORKLOADS if k != "int3_r2_fp16_8k"
+                   for seed in ((0,) if k.startswith("sweep_") else (0, 1, 2))]
+
+
+@pytest.mark.parametrize("name,seed", FULL_SIZE_CASES)
+def test_workload_full_size_sampled(qa, oracle, name, seed):
     w = W.WORKLOADS[name]
-    log(f"workload {name} n={w.n} R={w.ranks}")
-    xs = W.inputs(w, seed=0, device="cuda")
+    log(f"workload {name} n={w.n} R={w.ranks} seed={seed}")
+    xs = W.inputs(w, seed=seed, device="cuda")
     packed, out, y = run_pipeline(qa, w, xs)
     # a second run must give identical bytes (determinism)
     packed2, out2, y2 = run_pipeline(qa, w, xs)
@@ -262,7 +267,7 @@ def test_workload_full_size_sampled(qa, oracle, name):
         yd = qa.qr_decode(w.out_fmt, out, w.n, w.dtype)
         assert torch.equal(y.view(torch.int16), yd.view(torch.int16))
     ntiles = w.n // 2048
-    rng = np.random.default_rng(ntiles)
+    rng = np.random.default_rng(ntiles + seed)
     tiles = sorted(set([0, 1, ntiles - 1, ntiles // 2] + list(rng.integers(0, ntiles, 60))))
     tb = oracle.packed_bytes(BITS[w.fmt], 2048)
     sel_v = torch.tensor(np.concatenate([np.arange(t * 2048, (t + 1) * 2048) for t in tiles]), device="cuda")

@@ -26,6 +26,9 @@ tiles):
   asym6_r8_fp16_32x1024x4096  the same inputs, asymmetric 4-bit reduce inputs
                            and an asymmetric 8-bit re-encoded sum.
   fp4_r8_fp16_32x1024x4096  the same inputs through the FP4 E2M1 block codec.
+  int4_r8_fp16_4x1024x4096  one rank's share of that reduce in the two-shot
+                           scheme: R = 8 segments of n / 8 = 4 x 1024 x 4096
+                           values (the same channel spread).
 
 Random numbers come from torch's seeded generators (Philox on the GPU, the CPU
 generator on the host); each (seed, workload, rank) gets its own stream seed.
@@ -97,6 +100,9 @@ WORKLOADS = {
                                            32 * 1024 * 4096, (32, 1024, 4096),
                                            channel_sigma=(0.01, 20.0), fmt_out="asym8",
                                            data_key="int4_r8_fp16_32x1024x4096"),
+    # one rank's share (n / 8 values from each of the 8 ranks) of the reduce above
+    "int4_r8_fp16_4x1024x4096": Workload("int4_r8_fp16_4x1024x4096", "int4", torch.float16, 8,
+                                         4 * 1024 * 4096, (4, 1024, 4096), channel_sigma=(0.01, 20.0)),
     # FP4 E2M1 block codec on the same activations
     "fp4_r8_fp16_32x1024x4096": Workload("fp4_r8_fp16_32x1024x4096", "fp4", torch.float16, 8,
                                          32 * 1024 * 4096, (32, 1024, 4096),
