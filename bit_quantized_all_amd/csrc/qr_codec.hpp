@@ -17,12 +17,19 @@
 //   zero   z = clamp(rint(-lo * e), 0, 2^b - 1), one byte per group
 //   code   q = clamp(rint(x * e) + z, 0, 2^b - 1), packed as the INT4 / INT8 codes
 //   decode = (q - z) * s, exact in fp32.
+// FP4 block codec (OCP MX E2M1 elements in the INT4 framework; the
+// QuickReduce MI355 blog's introduction names a hardware FP4 path there):
+//   scale  d = fp16(min(max|x| / 6, 65504)), e = fp32(1/d) (0 if d == 0)
+//   code   = the E2M1 value nearest to x * e (ties to even, saturating, sign
+//          kept), by the gfx950 scaled FP4 conversion with scale 1.0
+//   decode = value * d, exact in fp32.
 //
 // Work mapping: one lane owns one block (32 values), one 64-lane wave owns one
-// 2048-value tile.  The block maximum and the scale are computed once per
-// lane with no cross-lane traffic; the fp16/bf16 side of a tile is moved
-// through a wave-private LDS tile so that every global access is a coalesced
-// 16-byte access.  Nothing here is a contraction, so there is no MFMA.
+// 2048-value tile; a 128-value asymmetric group is four lanes (DPP quad
+// permutes).  The block maximum and the scale are computed once per lane; the
+// fp16/bf16 side of a tile, and 8-bit codes, move through wave-private LDS so
+// that every global access is a coalesced 16-byte access.  Nothing here is a
+// contraction, so there is no MFMA.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -1,6 +1,8 @@
 // qr_kernels.hpp -- gfx950 kernels and their launch helpers (the C ABI that
-// calls them is in qr_api.hip; mixed-format reduce instantiations are in
-// qr_reduce_mixed.hip).
+// calls them is in qr_api.hip; the instantiations are spread over
+// qr_api.hip (INT3/INT4/INT8), qr_reduce_mixed.hip (mixed INT formats),
+// qr_asym.hip (asymmetric formats) and qr_fp4.hip (FP4), so they build in
+// parallel).
 //
 // Three kernels, each with one 64-lane wave per 2048-value tile and one lane
 // per 32-value block (the codec itself is in qr_codec.hpp):
@@ -191,6 +193,8 @@ struct ReduceArgs {
 
 template <int BI, int BO, int DT, int R, bool WITH_Y>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
+  static_assert(Format<BI>::kAsym == Format<BO>::kAsym && Format<BI>::kFp4 == Format<BO>::kFp4,
+                "a reduce stays within one format family");
   // per wave: the fp16/bf16 output tile (WITH_Y) and / or the 2 KB staging
   // region of 8-bit codes, which reuses the output tile's space
   constexpr int kLdsChunks = WITH_Y ? kChunks : ((kStaged<BI> || kStaged<BO>) ? kChunks / 2 : 1);
@@ -231,8 +235,10 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
       }
       if (r == 0) {
         // fma(k, d, +0) is the exact product k * d up to the sign of a zero
-        // (+0 for -0), which no later step can observe: it lets the fp16
-        // halves of the asymmetric decode feed one mixed-precision FMA
+        // (+0 for -0); it lets the fp16 halves of the asymmetric decode feed
+        // one mixed-precision FMA.  Asymmetric inputs reduce only into an
+        // asymmetric format, whose code of +-0 is z either way, so no later
+        // step can observe the difference.
 #pragma unroll
         for (int i = 0; i < kBlockValues; ++i) {
           if constexpr (Format<BI>::kAsym)
