@@ -92,7 +92,8 @@ def ingest_pmc(fetch_csv, write_csv, workload):
                 if row["Counter_Name"] != counter:
                     continue
                 name = row["Kernel_Name"]
-                key = next((k for k, v in KERNEL_KEYS.items() if v in name), None)
+                # this library's kernels only (torch has a reduce_kernel of its own)
+                key = next((k for k, v in KERNEL_KEYS.items() if "qr::" + v in name), None)
                 if key is None and "copy" in name.lower():
                     key = "copy"
                 if key:
