@@ -174,3 +174,14 @@ def test_fp4_validation(L):
         assert redm(L, fi=fi, fo=fo) == qr.QR_ERR_UNSUPPORTED, (fi, fo)
     assert redm(L, fi=36, fo=36, out=A - 1152 + 16) == qr.QR_ERR_ALIAS
     assert redm(L, fi=36, fo=36, n=0, ranks=[0], out=0, y=0) == qr.QR_OK
+
+
+def test_too_many_tiles(L):
+    """A value count whose tile index would not fit the kernels' int is a size
+    error, before any HIP call (so fake pointers are fine)."""
+    n = 2048 * (1 << 31)
+    assert enc(L, n=n) == qr.QR_ERR_SIZE
+    assert dec(L, n=n) == qr.QR_ERR_SIZE
+    assert red(L, n=n) == qr.QR_ERR_SIZE
+    assert redm(L, n=n) == qr.QR_ERR_SIZE
+    assert enc(L, n=2048 * ((1 << 31) - 1), x=0) == qr.QR_ERR_ARG   # largest accepted count reaches the null check

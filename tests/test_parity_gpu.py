@@ -704,3 +704,42 @@ def test_grid_stride_loops(small_grid, oracle, fmt, dtype):
     wout, wy = oracle.reduce(fid, dtype, wr, n)
     assert np.array_equal(out.cpu().numpy(), wout) and np.array_equal(out2.cpu().numpy(), wout)
     assert np.array_equal(u16(yr), wy)
+
+
+@pytest.mark.parametrize("fmt", ["int3", "int4", "int8", "asym4", "asym8", "fp4"])
+def test_buffers_at_16_byte_offsets(qa, oracle, fmt):
+    """Every buffer (inputs, packed ranks, packed output, y) starts 16 bytes
+    into its allocation, so no tile is aligned beyond the documented 16
+    bytes: encode, decode and the R = 3 reduce still match the oracle."""
+    fid = BITS[fmt]
+    ntiles = 21
+    n = ntiles * 2048
+    pb = qa.qr_packed_bytes(fmt, n)
+    xs = [gen(k, "bf16", n, seed=900 + i) for i, k in enumerate(("normal", "scales", "outliers"))]
+    log(f"16-byte offsets {fmt}")
+
+    def at16(numel, dtype):
+        return torch.empty(numel + 16 // torch.tensor([], dtype=dtype).element_size(), dtype=dtype,
+                           device="cuda")[16 // torch.tensor([], dtype=dtype).element_size():]
+
+    xd = []
+    for x in xs:
+        t = at16(n, torch.bfloat16)
+        t.copy_(dev(x, torch.bfloat16))
+        xd.append(t)
+    packed = [at16(pb, torch.uint8) for _ in xs]
+    assert all(p.data_ptr() % 256 == 16 for p in packed)
+    for x, p in zip(xd, packed):
+        qa.qr_encode(fmt, x, p)
+    y = at16(n, torch.bfloat16)
+    qa.qr_decode(fmt, packed[1], n, torch.bfloat16, y=y)
+    out, yr = at16(pb, torch.uint8), at16(n, torch.bfloat16)
+    qa.qr_reduce_compressed(fmt, torch.bfloat16, packed, n, packed_out=out, y_out=yr)
+    torch.cuda.synchronize()
+    wr = [oracle.encode(fid, "bf16", x) for x in xs]
+    for r in range(3):
+        assert np.array_equal(packed[r].cpu().numpy(), wr[r]), r
+    assert np.array_equal(u16(y), oracle.decode(fid, "bf16", wr[1], n))
+    wout, wy = oracle.reduce(fid, "bf16", wr, n)
+    assert np.array_equal(out.cpu().numpy(), wout)
+    assert np.array_equal(u16(yr), wy)
