@@ -52,7 +52,31 @@ def lib():
 
 
 def _fmt(fmt):
-    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    if isinstance(fmt, str):
+        if fmt not in FORMATS:
+            raise ValueError(f"unknown format {fmt!r} (one of {sorted(FORMATS)})")
+        return FORMATS[fmt]
+    return int(fmt)
+
+
+def _need(t, nbytes, name):
+    """The library writes and reads raw device memory: a tensor must hold the
+    bytes the call touches (the C ABI cannot check sizes)."""
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, the call needs {nbytes}")
+
+
+def _same_device(tensors):
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on several devices: {sorted(map(str, devs))}")
+
+
+def _io(t, dtype, n, name):
+    if t.dtype != dtype:
+        raise ValueError(f"{name} is {t.dtype}, the call's dtype is {dtype}")
+    _need(t, 2 * int(n), name)
 
 
 def _dt(dtype):
@@ -91,6 +115,8 @@ def qr_encode(fmt, x, packed=None, stream=None):
     n = x.numel()
     if packed is None:
         packed = torch.empty(qr_packed_bytes(fmt, n), dtype=torch.uint8, device=x.device)
+    _same_device([x, packed])
+    _need(packed, qr_packed_bytes(fmt, n), "packed")
     _check("qr_encode", lib().qr_encode(_fmt(fmt), _dt(x.dtype), _dev(x, "x"), _dev(packed, "packed"),
                                         n, _stream(stream)))
     return packed
@@ -100,9 +126,21 @@ def qr_decode(fmt, packed, n, dtype, y=None, stream=None):
     """Decode ``n`` values of ``dtype`` from the packed device tensor."""
     if y is None:
         y = torch.empty(n, dtype=dtype, device=packed.device)
+    _same_device([packed, y])
+    _need(packed, qr_packed_bytes(fmt, n), "packed")
+    _io(y, dtype, n, "y")
     _check("qr_decode", lib().qr_decode(_fmt(fmt), _dt(dtype), _dev(packed, "packed"), _dev(y, "y"),
                                         int(n), _stream(stream)))
     return y
+
+
+def _check_reduce(fmt_in, fmt_out, dtype, ranks, n, packed_out, y_out):
+    _same_device(list(ranks) + [packed_out, y_out])
+    for r in ranks:
+        _need(r, qr_packed_bytes(fmt_in, n), "rank buffer")
+    _need(packed_out, qr_packed_bytes(fmt_out, n), "packed_out")
+    if y_out is not None:
+        _io(y_out, dtype, n, "y_out")
 
 
 def qr_reduce_compressed(fmt, dtype, ranks, n, packed_out=None, y_out=None, with_output=True,
@@ -113,6 +151,7 @@ def qr_reduce_compressed(fmt, dtype, ranks, n, packed_out=None, y_out=None, with
         packed_out = torch.empty(qr_packed_bytes(fmt, n), dtype=torch.uint8, device=dev)
     if y_out is None and with_output:
         y_out = torch.empty(n, dtype=dtype, device=dev)
+    _check_reduce(fmt, fmt, dtype, ranks, n, packed_out, y_out)
     arr = (ctypes.c_void_p * len(ranks))(*[_dev(r, "rank").value for r in ranks])
     _check("qr_reduce_compressed",
            lib().qr_reduce_compressed(_fmt(fmt), _dt(dtype), arr, len(ranks), _dev(packed_out, "packed_out"),
@@ -129,6 +168,7 @@ def qr_reduce_compressed_mixed(fmt_in, fmt_out, dtype, ranks, n, packed_out=None
         packed_out = torch.empty(qr_packed_bytes(fmt_out, n), dtype=torch.uint8, device=dev)
     if y_out is None and with_output:
         y_out = torch.empty(n, dtype=dtype, device=dev)
+    _check_reduce(fmt_in, fmt_out, dtype, ranks, n, packed_out, y_out)
     arr = (ctypes.c_void_p * len(ranks))(*[_dev(r, "rank").value for r in ranks])
     _check("qr_reduce_compressed_mixed",
            lib().qr_reduce_compressed_mixed(_fmt(fmt_in), _fmt(fmt_out), _dt(dtype), arr, len(ranks),

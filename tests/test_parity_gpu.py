@@ -743,3 +743,27 @@ def test_buffers_at_16_byte_offsets(qa, oracle, fmt):
     wout, wy = oracle.reduce(fid, "bf16", wr, n)
     assert np.array_equal(out.cpu().numpy(), wout)
     assert np.array_equal(u16(yr), wy)
+
+
+def test_binding_rejects_short_or_mistyped_tensors(qa):
+    """The binding checks tensor byte sizes, the output dtype and the device
+    before calling the library (the C ABI takes raw pointers and cannot)."""
+    n = 4 * 2048
+    x = torch.zeros(n, dtype=torch.float16, device="cuda")
+    p = qa.qr_encode("int4", x)
+    with pytest.raises(ValueError):
+        qa.qr_encode("int4", x, torch.empty(4 * 1152 - 1, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        qa.qr_decode("int4", p, n, torch.float16, y=torch.empty(n - 1, dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError):
+        qa.qr_decode("int4", p, n, torch.float16, y=torch.empty(n, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        qa.qr_decode("int4", p[:100], n, torch.float16)
+    with pytest.raises(ValueError):
+        qa.qr_reduce_compressed("int4", torch.float16, [p, p[:-16]], n)
+    with pytest.raises(ValueError):
+        qa.qr_reduce_compressed_mixed("int4", "int8", torch.float16, [p], n,
+                                      packed_out=torch.empty(4 * 1152, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        qa.qr_encode("int5", x)
+    torch.cuda.synchronize()
