@@ -61,7 +61,7 @@ def build(out=LIB, extra=(), quiet=True, sources=None):
     return out
 
 
-TEST_HELPER_SRCS = [os.path.join(ROOT, "tests", "gpu_helpers", f) for f in ("scale_check.hip", "fp4_check.hip")]
+TEST_HELPER_SRCS = [os.path.join(ROOT, "tests", "gpu_helpers", f) for f in ("scale_check.hip", "fp4_check.hip", "asym_check.hip")]
 TEST_HELPER_LIB = os.path.join(ROOT, "tests", "gpu_helpers", "libscale_check.so")
 
 

@@ -767,3 +767,43 @@ def test_binding_rejects_short_or_mistyped_tensors(qa):
     with pytest.raises(ValueError):
         qa.qr_encode("int5", x)
     torch.cuda.synchronize()
+
+
+def test_asym_group_params_device_function(oracle):
+    """The library's asymmetric group parameters (scale bits, multiplier, zero
+    point) against the oracle's, for every positive finite fp16 h as the
+    ranges [0, h], [-h, 0] and [-h, h], 100,000 random fp16 ranges, bf16
+    ranges that saturate the scale or overflow hi - lo, and ranges with
+    infinite ends (fp16 sums that overflowed)."""
+    import ctypes
+    import os
+    lib = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gpu_helpers", "libscale_check.so")
+    L = ctypes.CDLL(lib)
+    L.qr_test_group_params.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 5 + [ctypes.c_int]
+    h = P.f16_value(np.arange(1, 0x7C00, dtype=np.uint16)).astype(np.float64)
+    rng = np.random.default_rng(77)
+    fin = P.f16_value(rng.integers(0, 0x7C00, size=(100000, 2)).astype(np.uint16)).astype(np.float64)
+    big = P.bf16_value(rng.integers(0x4700, 0x7F80, size=(2000, 2)).astype(np.uint16)).astype(np.float64)
+    inf = np.inf
+    lo = np.concatenate([np.zeros_like(h), -h, -h, -fin[:, 0], -big[:, 0], [-inf, 0.0, -inf, -0.0, 0.0, -1.0]])
+    hi = np.concatenate([h, np.zeros_like(h), h, fin[:, 1], big[:, 1], [0.0, inf, inf, 0.0, 0.0, inf]])
+    n = lo.size
+    lo_d = torch.tensor(lo, dtype=torch.float32, device="cuda")
+    hi_d = torch.tensor(hi, dtype=torch.float32, device="cuda")
+    log(f"asym group params on {n} ranges")
+    for bits, fid in ((4, 20), (8, 24)):
+        d = torch.zeros(n, dtype=torch.int32, device="cuda")
+        e = torch.zeros(n, dtype=torch.float32, device="cuda")
+        z = torch.zeros(n, dtype=torch.int32, device="cuda")
+        assert L.qr_test_group_params(fid, lo_d.data_ptr(), hi_d.data_ptr(), d.data_ptr(), e.data_ptr(),
+                                      z.data_ptr(), n) == 0
+        gd, ge, gz = d.cpu().numpy(), e.cpu().numpy(), z.cpu().numpy()
+        lo32, hi32 = lo.astype(np.float32), hi.astype(np.float32)
+        bad = []
+        for i in range(n):
+            wd, we, wz = oracle.group_params(bits, float(lo32[i]), float(hi32[i]))
+            if gd[i] != wd or gz[i] != wz or np.float32(ge[i]).tobytes() != np.float32(we).tobytes():
+                bad.append((float(lo32[i]), float(hi32[i]), hex(gd[i]), hex(wd), gz[i], wz))
+                if len(bad) > 5:
+                    break
+        assert not bad, (bits, bad)
