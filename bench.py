@@ -178,6 +178,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--values", type=int, default=None,
+                    help="override the workload's values per rank (a multiple of 2048), e.g. for a "
+                         "message-size sweep; the distribution and the rank count stay")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-mib", type=int, default=512,
@@ -211,6 +214,11 @@ def main():
 
     name = args.workload or W.BENCH_WORKLOAD
     w = W.WORKLOADS[name]
+    if args.values is not None:
+        if args.values <= 0 or args.values % 2048:
+            print("--values must be a positive multiple of 2048", file=sys.stderr)
+            sys.exit(2)
+        w = W.small(w, args.values)
     qa.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

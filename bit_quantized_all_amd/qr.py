@@ -6,6 +6,7 @@ current HIP stream.  The library must have been built
 (``bit_quantized_all_amd.build``); there is no fallback path.
 """
 import ctypes
+import functools
 import os
 
 import torch
@@ -68,9 +69,9 @@ def _need(t, nbytes, name):
 
 
 def _same_device(tensors):
-    devs = {t.device for t in tensors if t is not None}
+    devs = {t.get_device() for t in tensors if t is not None}
     if len(devs) > 1:
-        raise ValueError(f"tensors on several devices: {sorted(map(str, devs))}")
+        raise ValueError(f"tensors on several devices: {sorted(devs)}")
 
 
 def _io(t, dtype, n, name):
@@ -106,8 +107,13 @@ def qr_status_string(status):
     return lib().qr_status_string(int(status)).decode()
 
 
+@functools.lru_cache(maxsize=1024)
+def _packed_bytes(fmt_id, n):
+    return int(lib().qr_packed_bytes(fmt_id, n))
+
+
 def qr_packed_bytes(fmt, n):
-    return int(lib().qr_packed_bytes(_fmt(fmt), int(n)))
+    return _packed_bytes(_fmt(fmt), int(n))
 
 
 def qr_encode(fmt, x, packed=None, stream=None):

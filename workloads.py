@@ -162,6 +162,13 @@ def inputs(w, seed=0, device="cpu"):
 
 
 def small(w, n):
-    """The same workload with only `n` values per rank (for CPU-sized checks)."""
-    shape = (n // w.shape[-1], w.shape[-1]) if w.channel_sigma is not None else (n,)
+    """The same workload with only `n` values per rank (CPU-sized checks, size
+    sweeps); with per-channel spread the channel count stays when it divides n,
+    else every value is its own channel."""
+    if w.channel_sigma is None:
+        shape = (n,)
+    elif n % w.shape[-1] == 0:
+        shape = (n // w.shape[-1], w.shape[-1])
+    else:
+        shape = (1, n)
     return dataclasses.replace(w, n=n, shape=shape)
