@@ -203,7 +203,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the sharded "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the sharded "
               "two-shot exchange is described, not built); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
