@@ -66,6 +66,22 @@ TEST_HELPER_LIB = os.path.join(ROOT, "tests", "gpu_helpers", "libscale_check.so"
 
 
 SMALL_GRID_LIB = os.path.join(ROOT, "tests", "gpu_helpers", "libqr_smallgrid.so")
+ABI_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "abi_check.c")
+ABI_CHECK_BIN = os.path.join(ROOT, "tests", "c_abi", "abi_check")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_abi_check():
+    """A plain C program (gcc, no C++) that calls the C ABI of include/qr.h
+    against libqr.so, found through an rpath relative to the binary."""
+    cmd = ["gcc", "-std=c11", "-Wall", "-O2", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
+           "-I", os.path.join(ROOT, "include"), "-o", ABI_CHECK_BIN, ABI_CHECK_SRC,
+           "-L", HERE, "-lqr", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../bit_quantized_all_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    res = _run(cmd)
+    if res.returncode != 0:
+        raise RuntimeError(f"C ABI check build failed: {' '.join(cmd)}\n{res.stderr}")
+    return ABI_CHECK_BIN
 
 
 def build_test_helpers(quiet=True):
@@ -74,6 +90,7 @@ def build_test_helpers(quiet=True):
     workgroups, so that every kernel's grid-stride loop (and the encode's
     prefetch of the next tile) runs at small sizes."""
     build(out=SMALL_GRID_LIB, extra=["-DQR_MAX_GROUPS=3"], quiet=quiet)
+    build_abi_check()
     return build(out=TEST_HELPER_LIB, sources=TEST_HELPER_SRCS, quiet=quiet)
 
 

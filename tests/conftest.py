@@ -14,7 +14,8 @@ def pytest_configure(config):
     from bit_quantized_all_amd import build as hip_build
     if not os.path.exists(hip_build.LIB):
         hip_build.build()
-    if not (os.path.exists(hip_build.TEST_HELPER_LIB) and os.path.exists(hip_build.SMALL_GRID_LIB)):
+    if not all(os.path.exists(f) for f in (hip_build.TEST_HELPER_LIB, hip_build.SMALL_GRID_LIB,
+                                           hip_build.ABI_CHECK_BIN)):
         hip_build.build_test_helpers()
 
 

@@ -807,3 +807,16 @@ def test_asym_group_params_device_function(oracle):
                 if len(bad) > 5:
                     break
         assert not bad, (bits, bad)
+
+
+def test_c_abi_from_plain_c():
+    """tests/c_abi/abi_check.c, built with gcc against include/qr.h and
+    libqr.so, runs as a child process: exact round trips and exact two-rank
+    reductions for INT3/INT4/INT8 in fp16 and bf16, and rejected arguments."""
+    import os
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "abi_check")
+    log("plain C use of the ABI")
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "all checks hold" in res.stdout
