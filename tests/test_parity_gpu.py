@@ -820,3 +820,29 @@ def test_c_abi_from_plain_c():
     res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stdout + res.stderr
     assert "all checks hold" in res.stdout
+
+
+def test_calls_on_a_side_stream(qa, oracle):
+    """Every entry point enqueues on the stream it is given: the whole path on
+    a separately created stream (default priority), synchronized through that
+    stream alone, matches the oracle."""
+    n = 9 * 2048
+    xs = [gen("normal", "fp16", n, seed=40 + r) for r in range(3)]
+    side = torch.cuda.Stream()
+    xd = [dev(x, torch.float16) for x in xs]
+    torch.cuda.synchronize()
+    log("side stream")
+    with torch.cuda.stream(side):
+        packed = [torch.empty(qa.qr_packed_bytes("int3", n), dtype=torch.uint8, device="cuda") for _ in xs]
+        out = torch.empty(qa.qr_packed_bytes("int3", n), dtype=torch.uint8, device="cuda")
+        y = torch.empty(n, dtype=torch.float16, device="cuda")
+        yd = torch.empty(n, dtype=torch.float16, device="cuda")
+    for x, p in zip(xd, packed):
+        qa.qr_encode("int3", x, p, stream=side)
+    qa.qr_reduce_compressed("int3", torch.float16, packed, n, packed_out=out, y_out=y, stream=side)
+    qa.qr_decode("int3", out, n, torch.float16, y=yd, stream=side)
+    side.synchronize()
+    wr = [oracle.encode(3, "fp16", x) for x in xs]
+    wout, wy = oracle.reduce(3, "fp16", wr, n)
+    assert np.array_equal(out.cpu().numpy(), wout)
+    assert np.array_equal(u16(y), wy) and np.array_equal(u16(yd), wy)
