@@ -7,7 +7,6 @@ against it.  The real oracle passes every pin (``test_oracle_pins.py``); a
 mutant that passes them all means the pins have a blind spot.  Everything here
 runs on the CPU.
 """
-import os
 
 import pytest
 
