@@ -663,14 +663,14 @@ def pin_reduce_mixed_r1_composition(o, seed=9):
             exact = ((codes - qmax(a)).reshape(-1, 64, BLOCK) * f16_value(sb)[:, :, None]).ravel()
             zb = f16_bits(exact) if dtype == "fp16" else bf16_bits(exact)
             out, y = o.reduce_mixed(a, b, dtype, [p], n)
-            assert out.size == P_bytes(b, n)
+            assert out.size == sym_packed_bytes(b, n)
             assert np.array_equal(out, o.encode(b, dtype, zb)), (a, b, dtype)
             c2, s2 = unpack(b, out)
             ex2 = ((c2 - Qb).reshape(-1, 64, BLOCK) * f16_value(s2)[:, :, None]).ravel()
             assert np.array_equal(y, f16_bits(ex2) if dtype == "fp16" else bf16_bits(ex2)), (a, b, dtype)
 
 
-def P_bytes(bits, n):
+def sym_packed_bytes(bits, n):
     return n // TILE * tile_bytes(bits)
 
 
