@@ -67,7 +67,10 @@
  *      that rounds to zero is -0, code 8); decode = value * d, exact in fp32.
  *
  * All floating point is IEEE binary32 with round-to-nearest-even; build with
- * -O2 -ffp-contract=off and without -ffast-math.
+ * -O2 -ffp-contract=off and without -ffast-math.  binary32, not binary64:
+ * floating point here decides integers (codes, scales, zero points, the
+ * re-quantized sum), and those decisions are taken in the GPU kernels'
+ * precision; every decoded value and product is exact in binary32.
  */
 #include <math.h>
 #include <stddef.h>
