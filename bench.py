@@ -123,51 +123,94 @@ def ingest_pmc(fetch_csv, write_csv, workload):
     print(json.dumps(out, indent=1))
 
 
-def cpu_baseline(w, xs, out, y, seconds):
-    """The oracle (single-threaded C) on consecutive tiles of every rank, from
-    the first, until about `seconds` of oracle time; each chunk's inputs are
-    copied to the host outside the timed calls, and its outputs are compared
-    with the GPU's bytes for the same tiles."""
+def _oracle_pass(o, w, host, a, b):
+    """Oracle encode of tiles [a, b) of every rank, then its reduce (or decode)."""
+    sv = slice(a * 2048, b * 2048)
+    packed = [o.encode(FORMAT_IDS[w.fmt], w.io_dtype, h[sv]) for h in host]
+    if w.reduce:
+        return o.reduce_mixed(FORMAT_IDS[w.fmt], FORMAT_IDS[w.out_fmt], w.io_dtype, packed, (b - a) * 2048)
+    return None, o.decode(FORMAT_IDS[w.fmt], w.io_dtype, packed[0], (b - a) * 2048)
+
+
+def cpu_threads():
+    """Host threads for the threaded oracle leg: the usable CPUs, at most 16."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return max(1, min(16, usable))
+
+
+def cpu_baseline(w, xs, out, y, seconds, threads):
+    """The oracle (plain C through ctypes, which releases the GIL) on the first
+    tiles of every rank buffer, sized so that one single-threaded pass takes
+    about seconds / 5.  Two legs, each the median of 5 passes: one thread, then
+    the same tiles split into contiguous ranges over `threads` threads.  The
+    inputs are copied to the host before any timing.  The single-threaded
+    outputs are compared with the GPU's bytes for the same tiles, and the
+    threaded outputs with the single-threaded ones."""
+    import statistics
+    import threading
+
     import numpy as np
     import torch
 
     import oracle
 
     o = oracle.default()
-    bits = FORMAT_IDS[w.fmt]
-    obits = FORMAT_IDS[w.out_fmt]
     tb = TILE_BYTES[w.out_fmt]
     ntiles = w.n // 2048
-    chunk = 16
-    done = 0
-    ok = True
-    busy = 0.0
-    while done + chunk <= ntiles and (busy < seconds or done == 0):
-        sv = slice(done * 2048, (done + chunk) * 2048)
-        sb = slice(done * tb, (done + chunk) * tb)
-        host = [x[sv].view(torch.int16).cpu().numpy().view(np.uint16) for x in xs]
+    probe = min(16, ntiles)
+    host = [x[:probe * 2048].view(torch.int16).cpu().numpy().view(np.uint16) for x in xs]
+    t0 = time.perf_counter()
+    _oracle_pass(o, w, host, 0, probe)
+    per_tile = (time.perf_counter() - t0) / probe
+    tiles = max(probe, min(ntiles, int(seconds / 5 / per_tile) // 16 * 16))
+    host = [x[:tiles * 2048].view(torch.int16).cpu().numpy().view(np.uint16) for x in xs]
+
+    single = []
+    for _ in range(5):
         t0 = time.perf_counter()
-        packed = [o.encode(bits, w.io_dtype, h) for h in host]
-        if w.reduce:
-            po, yo = o.reduce_mixed(bits, obits, w.io_dtype, packed, chunk * 2048)
-        else:
-            po, yo = None, o.decode(bits, w.io_dtype, packed[0], chunk * 2048)
-        busy += time.perf_counter() - t0
-        if po is not None:
-            ok &= bool(np.array_equal(po, out[sb].cpu().numpy()))
-        ok &= bool(np.array_equal(yo, y[sv].view(torch.int16).cpu().numpy().view(np.uint16)))
-        done += chunk
-    gbs = w.ranks * done * 2048 * 2 / busy / 1e9
-    sample = (f"first {done} tiles ({done * 2048} values) of each of the {w.ranks} rank buffers of "
-              f"{w.name}: oracle encode x{w.ranks} + " + ("reduce with decode" if w.reduce else "decode")
-              + f", {busy:.1f} s of oracle time, one thread")
+        po, yo = _oracle_pass(o, w, host, 0, tiles)
+        single.append(time.perf_counter() - t0)
+    ok = bool(np.array_equal(yo, y[:tiles * 2048].view(torch.int16).cpu().numpy().view(np.uint16)))
+    if po is not None:
+        ok &= bool(np.array_equal(po, out[:tiles * tb].cpu().numpy()))
+
+    threads = max(1, min(threads, tiles))
+    bounds = [tiles * k // threads for k in range(threads + 1)]
+    multi = []
+    for _ in range(5):
+        parts = [None] * threads
+
+        def work(k):
+            parts[k] = _oracle_pass(o, w, host, bounds[k], bounds[k + 1])
+
+        pool = [threading.Thread(target=work, args=(k,)) for k in range(threads)]
+        t0 = time.perf_counter()
+        for t in pool:
+            t.start()
+        for t in pool:
+            t.join()
+        multi.append(time.perf_counter() - t0)
+    ok &= bool(np.array_equal(np.concatenate([p[1] for p in parts]), yo))
+    if po is not None:
+        ok &= bool(np.array_equal(np.concatenate([p[0] for p in parts]), po))
+
+    fp16_bytes = w.ranks * tiles * 2048 * 2
+    t1, tn = statistics.median(single), statistics.median(multi)
+    what = (f"first {tiles} tiles ({tiles * 2048} values) of each of the {w.ranks} rank buffers of "
+            f"{w.name}: oracle encode x{w.ranks} + " + ("reduce with decode" if w.reduce else "decode")
+            + f"; median of 5 passes; one pass takes {t1:.2f} s on one thread")
     model = None
     try:
         with open("/proc/cpuinfo") as f:
             model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
     except OSError:
         pass
-    return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": sample,
+    return {"value": round(fp16_bytes / tn / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": what + f", {tn:.3f} s on {threads} threads over contiguous tile ranges",
+            "single_thread": {"value": round(fp16_bytes / t1 / 1e9, 5), "unit": "GB/s", "cores": 1},
             "cpu_model": model, "host_cpus": os.cpu_count()}, ok
 
 
@@ -181,7 +224,11 @@ def main():
     ap.add_argument("--values", type=int, default=None,
                     help="override the workload's values per rank (a multiple of 2048), e.g. for a "
                          "message-size sweep; the distribution and the rank count stay")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="single-threaded oracle time of the 5 timed passes together (the threaded "
+                         "leg adds as much CPU time again)")
+    ap.add_argument("--cpu-threads", type=int, default=None,
+                    help="threads of the threaded oracle leg (default: usable CPUs, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-mib", type=int, default=512,
                     help="rotate through enough identical buffer sets (inputs, packed, outputs) that "
@@ -379,7 +426,7 @@ def main():
     if copy_ref:
         result["copy_ref"] = copy_ref
     if not args.no_cpu_baseline:
-        cb, ok = cpu_baseline(w, xs, out, y, args.cpu_seconds)
+        cb, ok = cpu_baseline(w, xs, out, y, args.cpu_seconds, args.cpu_threads or cpu_threads())
         result["cpu_baseline"] = cb
         result["parity_sample"] = ok
     print(json.dumps(result), flush=True)
