@@ -331,6 +331,18 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
 
+    # the same K steps again, with an event between consecutive steps -> median step
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        run_steps[i % nsets]()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    ms_median = per_step[args.steps // 2] if args.steps % 2 else \
+        0.5 * (per_step[args.steps // 2 - 1] + per_step[args.steps // 2])
+
     # timed region 2: each kernel alone, K steps' worth of back-to-back launches
     # between two events on the launch stream -> average launch duration
     def timed(fn, launches):
@@ -407,6 +419,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_median": round(ms_median, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

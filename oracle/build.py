@@ -14,9 +14,10 @@ LIB = os.path.join(HERE, "libqr_oracle.so")
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math"]
 
 
-def build(src=SRC, out=LIB, cc="gcc", quiet=True):
-    """Compile ``src`` into the shared library ``out``; returns ``out``."""
-    cmd = [cc, *CFLAGS, "-o", out, src, "-lm"]
+def build(src=SRC, out=LIB, cc="gcc", quiet=True, extra=()):
+    """Compile ``src`` into the shared library ``out`` (``extra``: more compiler
+    flags, e.g. sanitizers); returns ``out``."""
+    cmd = [cc, *CFLAGS, *extra, "-o", out, src, "-lm"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"oracle build failed: {' '.join(cmd)}\n{res.stderr}")
