@@ -61,6 +61,11 @@ namespace qr {
 #ifndef QR_RED_LOADS_FIRST
 #define QR_RED_LOADS_FIRST 1
 #endif
+// registers per lane that the R blocks of codes and scales may hold before
+// the decode starts; above it the loads are left to the scheduler
+#ifndef QR_RED_LOADS_FIRST_REGS
+#define QR_RED_LOADS_FIRST_REGS 128
+#endif
 constexpr int kWavesPerGroup = QR_WAVES_PER_GROUP;
 constexpr int kThreads = kWave * kWavesPerGroup;
 constexpr int kMaxGroups = QR_MAX_GROUPS;
@@ -210,9 +215,12 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     uint32_t sc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) load_block<BI, QR_RED_NT_LOAD>(a.ranks[r] + toff, lane, blk[r], sc[r]);
-#if QR_RED_LOADS_FIRST
-    __builtin_amdgcn_sched_barrier(0);  // every rank's loads in flight before decoding starts
-#endif
+    // every rank's loads in flight before decoding starts, where R blocks of
+    // codes fit in registers beside the sum and the decode temporaries (with
+    // 8-bit codes at R = 15 and 16 they would not: the compiler then parks
+    // registers in AGPRs and the kernel drops to one wave per SIMD)
+    if constexpr (QR_RED_LOADS_FIRST && R * (int)(sizeof(Block<BI>) / 4 + 1) <= QR_RED_LOADS_FIRST_REGS)
+      __builtin_amdgcn_sched_barrier(0);
     // exact decode of every rank, fp32 sum in rank order: s = y_0, s = s + y_r
     float s[kBlockValues];
 #pragma unroll
