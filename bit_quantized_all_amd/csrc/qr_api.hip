@@ -145,7 +145,7 @@ const char* qr_status_string(qr_status s) {
   switch (s) {
     case QR_OK: return "ok";
     case QR_ERR_ARG: return "invalid argument (null pointer or rank count)";
-    case QR_ERR_SIZE: return "value count is not a multiple of 2048";
+    case QR_ERR_SIZE: return "value count is not a multiple of 2048 or exceeds 2^31 tiles";
     case QR_ERR_ALIGN: return "buffer pointer is not 16-byte aligned";
     case QR_ERR_UNSUPPORTED: return "unsupported format or dtype";
     case QR_ERR_ALIAS: return "output buffer overlaps another buffer";

@@ -356,58 +356,63 @@ inline dim3 grid_for(size_t ntiles) {
   return dim3((unsigned)g);
 }
 
+// Launches a kernel with kThreads threads per workgroup and returns the status
+// of that launch itself (hipGetLastError could also report an earlier failure
+// of an unrelated call on the same thread).  The parameter types come from the
+// kernel alone, so each argument is converted to its parameter's type.
+template <typename... P>
+struct Launch {
+  void (*kernel)(P...);
+  qr_status operator()(dim3 grid, hipStream_t st, P... args) const {
+    void* argv[] = {static_cast<void*>(&args)...};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(kThreads), argv, 0, st) ==
+                   hipSuccess
+               ? QR_OK
+               : QR_ERR_HIP;
+  }
+};
+template <typename... P>
+Launch<P...> launch(void (*kernel)(P...)) {
+  return {kernel};
+}
+
 template <int BITS>
 qr_status launch_encode(int dt, const void* x, void* p, size_t ntiles, hipStream_t st) {
   const dim3 grid = grid_for((ntiles + QR_ENC_TILES_PER_WAVE - 1) / QR_ENC_TILES_PER_WAVE);
-  if (dt == kFp16)
-    hipLaunchKernelGGL((encode_kernel<BITS, kFp16>), grid, dim3(kThreads), 0, st,
-                       (const uint8_t*)x, (uint8_t*)p, (int)ntiles);
-  else
-    hipLaunchKernelGGL((encode_kernel<BITS, kBf16>), grid, dim3(kThreads), 0, st,
-                       (const uint8_t*)x, (uint8_t*)p, (int)ntiles);
-  return hipGetLastError() == hipSuccess ? QR_OK : QR_ERR_HIP;
+  auto k = dt == kFp16 ? launch(encode_kernel<BITS, kFp16>) : launch(encode_kernel<BITS, kBf16>);
+  return k(grid, st, (const uint8_t*)x, (uint8_t*)p, (int)ntiles);
 }
 
 template <int BITS>
 qr_status launch_decode(int dt, const void* p, void* y, size_t ntiles, hipStream_t st) {
-  const dim3 grid = grid_for(ntiles);
-  if (dt == kFp16)
-    hipLaunchKernelGGL((decode_kernel<BITS, kFp16>), grid, dim3(kThreads), 0, st,
-                       (const uint8_t*)p, (uint8_t*)y, (int)ntiles);
-  else
-    hipLaunchKernelGGL((decode_kernel<BITS, kBf16>), grid, dim3(kThreads), 0, st,
-                       (const uint8_t*)p, (uint8_t*)y, (int)ntiles);
-  return hipGetLastError() == hipSuccess ? QR_OK : QR_ERR_HIP;
+  auto k = dt == kFp16 ? launch(decode_kernel<BITS, kFp16>) : launch(decode_kernel<BITS, kBf16>);
+  return k(grid_for(ntiles), st, (const uint8_t*)p, (uint8_t*)y, (int)ntiles);
 }
 
 template <int BI, int BO, int DT, int R>
-void launch_reduce_r(const ReduceArgs& a, dim3 grid, hipStream_t st) {
-  if (a.y)
-    hipLaunchKernelGGL((reduce_kernel<BI, BO, DT, R, true>), grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((reduce_kernel<BI, BO, DT, R, false>), grid, dim3(kThreads), 0, st, a);
+qr_status launch_reduce_r(const ReduceArgs& a, dim3 grid, hipStream_t st) {
+  auto k = a.y ? launch(reduce_kernel<BI, BO, DT, R, true>) : launch(reduce_kernel<BI, BO, DT, R, false>);
+  return k(grid, st, a);
 }
 
 template <int BI, int BO, int DT>
-void launch_reduce_dt(const ReduceArgs& a, dim3 grid, hipStream_t st) {
+qr_status launch_reduce_dt(const ReduceArgs& a, dim3 grid, hipStream_t st) {
   switch (a.R) {
 #define QR_RANK_CASE(r) \
-  case r: launch_reduce_r<BI, BO, DT, r>(a, grid, st); break;
+  case r: return launch_reduce_r<BI, BO, DT, r>(a, grid, st);
     QR_RANK_CASE(1) QR_RANK_CASE(2) QR_RANK_CASE(3) QR_RANK_CASE(4)
     QR_RANK_CASE(5) QR_RANK_CASE(6) QR_RANK_CASE(7) QR_RANK_CASE(8)
     QR_RANK_CASE(9) QR_RANK_CASE(10) QR_RANK_CASE(11) QR_RANK_CASE(12)
     QR_RANK_CASE(13) QR_RANK_CASE(14) QR_RANK_CASE(15) QR_RANK_CASE(16)
 #undef QR_RANK_CASE
-    default: break;  // R was validated to be in [1, QR_MAX_RANKS]
+    default: return QR_ERR_ARG;  // R is validated to be in [1, QR_MAX_RANKS] before this
   }
 }
 
 template <int BI, int BO>
 qr_status launch_reduce(int dt, const ReduceArgs& a, hipStream_t st) {
   const dim3 grid = grid_for((size_t)a.ntiles);
-  if (dt == kFp16) launch_reduce_dt<BI, BO, kFp16>(a, grid, st);
-  else launch_reduce_dt<BI, BO, kBf16>(a, grid, st);
-  return hipGetLastError() == hipSuccess ? QR_OK : QR_ERR_HIP;
+  return dt == kFp16 ? launch_reduce_dt<BI, BO, kFp16>(a, grid, st) : launch_reduce_dt<BI, BO, kBf16>(a, grid, st);
 }
 
 // Reduce with input format != output format (instantiated in qr_reduce_mixed.hip,

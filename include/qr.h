@@ -84,11 +84,11 @@ extern "C" {
 typedef enum {
   QR_OK = 0,
   QR_ERR_ARG = 1,         /* null pointer, R out of [1, QR_MAX_RANKS] */
-  QR_ERR_SIZE = 2,        /* n not a multiple of 2048 */
+  QR_ERR_SIZE = 2,        /* n not a multiple of 2048, or more than 2^31 - 1 tiles */
   QR_ERR_ALIGN = 3,       /* a buffer pointer is not 16-byte aligned */
   QR_ERR_UNSUPPORTED = 4, /* unknown format or dtype */
   QR_ERR_ALIAS = 5,       /* an output overlaps an input or the other output */
-  QR_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+  QR_ERR_HIP = 6          /* the HIP runtime refused the kernel launch */
 } qr_status;
 
 /* Symmetric 32-value block formats are named by their code width, the

@@ -867,3 +867,27 @@ def test_repeat_runs_are_bit_identical(qa, fmt):
                                                  yd.view(torch.int16).cpu()])
     for a, b in zip(*runs):
         assert torch.equal(a, b)
+
+
+def test_earlier_unrelated_hip_error_is_not_reported(qa, oracle):
+    """A call returns the status of its own launch: an error that an earlier,
+    unrelated HIP call left on the thread (here a host-side invalid device
+    number, no GPU work involved) does not fail the call."""
+    import ctypes
+
+    n = 4 * 2048
+    xb = gen("normal", "fp16", n, seed=5)
+    x = dev(xb, torch.float16)
+    packed = torch.empty(qa.qr_packed_bytes("int4", n), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    hip = ctypes.CDLL("libamdhip64.so.7")   # the runtime already loaded in this process
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    hip.hipGetLastError.restype = ctypes.c_int
+    log("stale HIP error")
+    assert hip.hipSetDevice(1 << 20) != 0
+    try:
+        qa.qr_encode("int4", x, packed)
+    finally:
+        hip.hipGetLastError()   # clear it before torch's next launch check
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy(), oracle.encode(4, "fp16", xb))
