@@ -891,3 +891,39 @@ def test_earlier_unrelated_hip_error_is_not_reported(qa, oracle):
         hip.hipGetLastError()   # clear it before torch's next launch check
     torch.cuda.synchronize()
     assert np.array_equal(packed.cpu().numpy(), oracle.encode(4, "fp16", xb))
+
+
+@pytest.mark.parametrize("fmt", ["int3", "int8", "asym8", "fp4"])
+def test_buffers_beyond_4_gib(qa, oracle, fmt):
+    """Byte offsets past 2^32: two ranks of 2,050,131 tiles (4,198,668,288
+    bf16 values, 8.4 GB each, a count that is not a multiple of the four
+    tiles of a workgroup), so that the inputs and outputs, and the packed
+    buffers of the 8-bit formats, extend past 4 GiB.  The encode, the fused
+    reduce and the standalone decode are compared with the oracle on sampled
+    tiles, among them the tiles next to the 4 GiB mark of each buffer."""
+    ntiles = 2_050_131
+    n = ntiles * 2048
+    fid = BITS[fmt]
+    tb = oracle.packed_bytes(fid, 2048)
+    log(f"beyond 4 GiB {fmt} n={n}")
+    g = torch.Generator(device="cuda").manual_seed(11)
+    xs = [torch.randn(n, dtype=torch.bfloat16, device="cuda", generator=g) for _ in range(2)]
+    packed = [qa.qr_encode(fmt, x) for x in xs]
+    out, y = qa.qr_reduce_compressed(fmt, torch.bfloat16, packed, n)
+    yd = qa.qr_decode(fmt, out, n, torch.bfloat16)
+    torch.cuda.synchronize()
+    edge = {(1 << 32) // 4096 - 1, (1 << 32) // 4096, (1 << 32) // tb, (1 << 32) // tb + 1}
+    rng = np.random.default_rng(3)
+    tiles = sorted(t for t in edge | {0, ntiles - 1} | set(rng.integers(0, ntiles, 24).tolist())
+                   if t < ntiles)
+    for t in tiles:
+        xv = [u16(x[t * 2048:(t + 1) * 2048]) for x in xs]
+        pv = [p[t * tb:(t + 1) * tb].cpu().numpy() for p in packed]
+        for r in range(2):
+            assert np.array_equal(pv[r], oracle.encode(fid, "bf16", xv[r])), (fmt, t, r)
+        wout, wy = oracle.reduce(fid, "bf16", pv, 2048)
+        assert np.array_equal(out[t * tb:(t + 1) * tb].cpu().numpy(), wout), (fmt, t)
+        assert np.array_equal(u16(y[t * 2048:(t + 1) * 2048]), wy), (fmt, t)
+        assert np.array_equal(u16(yd[t * 2048:(t + 1) * 2048]), wy), (fmt, t)
+    del xs, packed, out, y, yd
+    torch.cuda.empty_cache()
