@@ -60,42 +60,46 @@ def _fmt(fmt):
     return int(fmt)
 
 
-def _need(t, nbytes, name):
-    """The library writes and reads raw device memory: a tensor must hold the
-    bytes the call touches (the C ABI cannot check sizes)."""
-    have = t.numel() * t.element_size()
-    if have < nbytes:
-        raise ValueError(f"{name} holds {have} bytes, the call needs {nbytes}")
-
-
-def _same_device(tensors):
-    devs = {t.get_device() for t in tensors if t is not None}
-    if len(devs) > 1:
-        raise ValueError(f"tensors on several devices: {sorted(devs)}")
-
-
-def _io(t, dtype, n, name):
-    if t.dtype != dtype:
-        raise ValueError(f"{name} is {t.dtype}, the call's dtype is {dtype}")
-    _need(t, 2 * int(n), name)
-
-
 def _dt(dtype):
     if dtype not in DTYPES:
         raise ValueError(f"unsupported dtype {dtype}")
     return DTYPES[dtype]
 
 
-def _stream(stream):
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
-
-
-def _dev(t, name):
+def _ptr(t, name, nbytes, device=None):
+    """Device address of a contiguous device tensor that holds at least
+    ``nbytes`` bytes and lives on ``device`` (an index; None takes t's).  The
+    library reads and writes raw device memory, so the binding checks here what
+    the C ABI cannot: the tensor's kind, size and device."""
     if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
         raise ValueError(f"{name} must be a contiguous device tensor")
-    return ctypes.c_void_p(t.data_ptr())
+    if device is not None and t.get_device() != device:
+        raise ValueError(f"{name} is on device {t.get_device()}, the call's tensors are on device {device}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, the call needs {nbytes}")
+    return t.data_ptr()
+
+
+def _io(t, dtype, n, name, device):
+    if t.dtype != dtype:
+        raise ValueError(f"{name} is {t.dtype}, the call's dtype is {dtype}")
+    return _ptr(t, name, 2 * int(n), device)
+
+
+# The current stream's raw handle without building a torch.cuda.Stream object
+# (that costs microseconds per call); the public route where it is missing.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, device):
+    """HIP stream handle: the given stream, else the current stream of the
+    device that holds the call's tensors."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(device)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _check(fn, status):
@@ -118,67 +122,59 @@ def qr_packed_bytes(fmt, n):
 
 def qr_encode(fmt, x, packed=None, stream=None):
     """Encode the fp16/bf16 device tensor ``x``; returns the packed uint8 tensor."""
-    n = x.numel()
+    fid, n = _fmt(fmt), x.numel()
+    pb = _packed_bytes(fid, n)
     if packed is None:
-        packed = torch.empty(qr_packed_bytes(fmt, n), dtype=torch.uint8, device=x.device)
-    _same_device([x, packed])
-    _need(packed, qr_packed_bytes(fmt, n), "packed")
-    _check("qr_encode", lib().qr_encode(_fmt(fmt), _dt(x.dtype), _dev(x, "x"), _dev(packed, "packed"),
-                                        n, _stream(stream)))
+        packed = torch.empty(pb, dtype=torch.uint8, device=x.device)
+    xp = _ptr(x, "x", 0)
+    dev = x.get_device()
+    pp = _ptr(packed, "packed", pb, dev)
+    _check("qr_encode", lib().qr_encode(fid, _dt(x.dtype), xp, pp, n, _stream(stream, dev)))
     return packed
 
 
 def qr_decode(fmt, packed, n, dtype, y=None, stream=None):
     """Decode ``n`` values of ``dtype`` from the packed device tensor."""
+    fid, n = _fmt(fmt), int(n)
     if y is None:
         y = torch.empty(n, dtype=dtype, device=packed.device)
-    _same_device([packed, y])
-    _need(packed, qr_packed_bytes(fmt, n), "packed")
-    _io(y, dtype, n, "y")
-    _check("qr_decode", lib().qr_decode(_fmt(fmt), _dt(dtype), _dev(packed, "packed"), _dev(y, "y"),
-                                        int(n), _stream(stream)))
+    pp = _ptr(packed, "packed", _packed_bytes(fid, n))
+    dev = packed.get_device()
+    yp = _io(y, dtype, n, "y", dev)
+    _check("qr_decode", lib().qr_decode(fid, _dt(dtype), pp, yp, n, _stream(stream, dev)))
     return y
 
 
-def _check_reduce(fmt_in, fmt_out, dtype, ranks, n, packed_out, y_out):
-    _same_device(list(ranks) + [packed_out, y_out])
-    for r in ranks:
-        _need(r, qr_packed_bytes(fmt_in, n), "rank buffer")
-    _need(packed_out, qr_packed_bytes(fmt_out, n), "packed_out")
-    if y_out is not None:
-        _io(y_out, dtype, n, "y_out")
+def _reduce(fn, fmt_in, fmt_out, dtype, ranks, n, packed_out, y_out, with_output, stream):
+    fi, fo, n = _fmt(fmt_in), _fmt(fmt_out), int(n)
+    if not ranks:
+        raise ValueError("no rank buffers")
+    dev = ranks[0].get_device()
+    pin, pout = _packed_bytes(fi, n), _packed_bytes(fo, n)
+    if packed_out is None:
+        packed_out = torch.empty(pout, dtype=torch.uint8, device=ranks[0].device)
+    if y_out is None and with_output:
+        y_out = torch.empty(n, dtype=dtype, device=ranks[0].device)
+    arr = (ctypes.c_void_p * len(ranks))(*[_ptr(r, "rank buffer", pin, dev) for r in ranks])
+    op = _ptr(packed_out, "packed_out", pout, dev)
+    yp = _io(y_out, dtype, n, "y_out", dev) if y_out is not None else None
+    if fn == "qr_reduce_compressed":
+        st = lib().qr_reduce_compressed(fi, _dt(dtype), arr, len(ranks), op, yp, n, _stream(stream, dev))
+    else:
+        st = lib().qr_reduce_compressed_mixed(fi, fo, _dt(dtype), arr, len(ranks), op, yp, n,
+                                              _stream(stream, dev))
+    _check(fn, st)
+    return packed_out, y_out
 
 
 def qr_reduce_compressed(fmt, dtype, ranks, n, packed_out=None, y_out=None, with_output=True,
                          stream=None):
     """Reduce R packed rank buffers; returns (packed_out, y_out or None)."""
-    dev = ranks[0].device
-    if packed_out is None:
-        packed_out = torch.empty(qr_packed_bytes(fmt, n), dtype=torch.uint8, device=dev)
-    if y_out is None and with_output:
-        y_out = torch.empty(n, dtype=dtype, device=dev)
-    _check_reduce(fmt, fmt, dtype, ranks, n, packed_out, y_out)
-    arr = (ctypes.c_void_p * len(ranks))(*[_dev(r, "rank").value for r in ranks])
-    _check("qr_reduce_compressed",
-           lib().qr_reduce_compressed(_fmt(fmt), _dt(dtype), arr, len(ranks), _dev(packed_out, "packed_out"),
-                                      _dev(y_out, "y_out") if y_out is not None else None,
-                                      int(n), _stream(stream)))
-    return packed_out, y_out
+    return _reduce("qr_reduce_compressed", fmt, fmt, dtype, ranks, n, packed_out, y_out, with_output, stream)
 
 
 def qr_reduce_compressed_mixed(fmt_in, fmt_out, dtype, ranks, n, packed_out=None, y_out=None,
                                with_output=True, stream=None):
     """Inputs packed in fmt_in, re-encoded sum in fmt_out; returns (packed_out, y_out or None)."""
-    dev = ranks[0].device
-    if packed_out is None:
-        packed_out = torch.empty(qr_packed_bytes(fmt_out, n), dtype=torch.uint8, device=dev)
-    if y_out is None and with_output:
-        y_out = torch.empty(n, dtype=dtype, device=dev)
-    _check_reduce(fmt_in, fmt_out, dtype, ranks, n, packed_out, y_out)
-    arr = (ctypes.c_void_p * len(ranks))(*[_dev(r, "rank").value for r in ranks])
-    _check("qr_reduce_compressed_mixed",
-           lib().qr_reduce_compressed_mixed(_fmt(fmt_in), _fmt(fmt_out), _dt(dtype), arr, len(ranks),
-                                            _dev(packed_out, "packed_out"),
-                                            _dev(y_out, "y_out") if y_out is not None else None,
-                                            int(n), _stream(stream)))
-    return packed_out, y_out
+    return _reduce("qr_reduce_compressed_mixed", fmt_in, fmt_out, dtype, ranks, n, packed_out, y_out,
+                   with_output, stream)
