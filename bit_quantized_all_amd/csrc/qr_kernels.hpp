@@ -66,9 +66,23 @@ namespace qr {
 #ifndef QR_RED_LOADS_FIRST_REGS
 #define QR_RED_LOADS_FIRST_REGS 128
 #endif
+// Encode workgroups resident on one CU at a time.  Every encode wave has its
+// whole 4 KB input tile in flight at once; a full CU (8 workgroups, 32 waves)
+// keeps more requests outstanding than HBM serves best, and 5 workgroups
+// (20 waves) measured fastest: per 134M-value fp16 rank, INT4 56.9 -> 53.2 us,
+// INT3 53.9 -> 51.1 us, INT8 64.4 -> 62.6 us; 3 and 2 workgroups were slower.
+// The kernel sizes its LDS so that no more fit in the CU's 160 KB.
+#ifndef QR_ENC_GROUPS_PER_CU
+#define QR_ENC_GROUPS_PER_CU 5
+#endif
 constexpr int kWavesPerGroup = QR_WAVES_PER_GROUP;
 constexpr int kThreads = kWave * kWavesPerGroup;
 constexpr int kMaxGroups = QR_MAX_GROUPS;
+constexpr int kLdsBytesPerCU = 160 * 1024;
+// 16-byte LDS chunks per encode wave: the tile's kChunks, plus the unused
+// rest of the 1 / QR_ENC_GROUPS_PER_CU share of the CU's LDS
+constexpr int kEncLdsChunks = kLdsBytesPerCU / QR_ENC_GROUPS_PER_CU / (16 * kWavesPerGroup);
+static_assert(kEncLdsChunks >= kChunks, "the encode tile must fit in its LDS share");
 
 // ---------------------------------------------------------------------------
 // encode
@@ -77,7 +91,7 @@ constexpr int kMaxGroups = QR_MAX_GROUPS;
 template <int BITS, int DT>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restrict__ x,
                                                           uint8_t* __restrict__ packed, int ntiles) {
-  __shared__ u32x4 lds[kWavesPerGroup][kChunks];
+  __shared__ u32x4 lds[kWavesPerGroup][kEncLdsChunks];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
   u32x4* tl = lds[wave];
