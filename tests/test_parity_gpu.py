@@ -927,3 +927,42 @@ def test_buffers_beyond_4_gib(qa, oracle, fmt):
         assert np.array_equal(u16(yd[t * 2048:(t + 1) * 2048]), wy), (fmt, t)
     del xs, packed, out, y, yd
     torch.cuda.empty_cache()
+
+
+FAMILIES = {"int": ("int3", "int4", "int8"), "asym": ("asym4", "asym8"), "fp4": ("fp4",)}
+
+
+@pytest.mark.parametrize("block", range(6))
+def test_random_cases_match_oracle(qa, oracle, block):
+    """Seeded random cases across the whole surface: a format family, an input
+    and an output format within it, the dtype, R in [1, 16], a tile count in
+    [1, 300], and per rank one of the value families of the oracle's model
+    cross-check (heavy tails, blocks over the dtype's whole exponent range,
+    exact rounding ties for every format, zero / single / saturating /
+    subnormal blocks).  Encode, the fused reduce and the decode of its output
+    are compared with the oracle byte for byte."""
+    import test_oracle_model as TM
+
+    for case in range(20):
+        seed = 1000 * block + case
+        rng = np.random.default_rng(seed)
+        fam = FAMILIES[("int", "asym", "fp4")[rng.integers(3)]]
+        fi, fo = fam[rng.integers(len(fam))], fam[rng.integers(len(fam))]
+        dtype = ("fp16", "bf16")[rng.integers(2)]
+        R = int(rng.integers(1, 17))
+        ntiles = int(rng.integers(1, 301))
+        n = ntiles * 2048
+        kinds = [TM.FAMILIES[rng.integers(len(TM.FAMILIES))] for _ in range(R)]
+        log(f"random case seed={seed}: {fi}->{fo} {dtype} R={R} tiles={ntiles} {kinds}")
+        xs = [TM.family(k, dtype, rng, tiles=ntiles) for k in kinds]
+        packed = [qa.qr_encode(fi, dev(x, DT[dtype])) for x in xs]
+        out, y = qa.qr_reduce_compressed_mixed(fi, fo, DT[dtype], packed, n)
+        yd = qa.qr_decode(fo, out, n, DT[dtype])
+        torch.cuda.synchronize()
+        wr = [oracle.encode(BITS[fi], dtype, x) for x in xs]
+        for r in range(R):
+            assert np.array_equal(packed[r].cpu().numpy(), wr[r]), (seed, "encode", r)
+        wout, wy = oracle.reduce_mixed(BITS[fi], BITS[fo], dtype, wr, n)
+        assert np.array_equal(out.cpu().numpy(), wout), (seed, "packed_out")
+        assert np.array_equal(u16(y), wy), (seed, "y_out")
+        assert np.array_equal(u16(yd), oracle.decode(BITS[fo], dtype, wout, n)), (seed, "decode")
