@@ -52,7 +52,8 @@ constexpr int kChunks = kTileValues * 2 / 16;  // 16-byte chunks of one fp16/bf1
 enum { kFp16 = 0, kBf16 = 1 };
 
 // Formats are named by their qr_format value: 3, 4, 8 (symmetric, 32-value
-// blocks) and 20, 24 (asymmetric, 128-value groups, 4- and 8-bit codes).
+// blocks), 20, 24 (asymmetric, 128-value groups, 4- and 8-bit codes) and 36
+// (FP4 E2M1 codes in 32-value blocks).
 template <int F>
 struct Format;
 template <>
