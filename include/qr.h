@@ -59,8 +59,9 @@
  *   decode: y = value(code) * d, exact in fp32, rounded to the I/O dtype.
  *
  * Conventions for every call:
- *   - `n` counts values and must be a multiple of 2048 (QR_ERR_SIZE otherwise);
- *     n == 0 is a valid empty call that launches nothing and returns QR_OK.
+ *   - `n` counts values and must be a multiple of 2048, of at most 2^31 - 1
+ *     tiles (QR_ERR_SIZE otherwise); n == 0 is a valid empty call that
+ *     launches nothing and returns QR_OK.
  *   - Buffer pointers are DEVICE pointers (hipMalloc or the PyTorch caching
  *     allocator), 16-byte aligned (QR_ERR_ALIGN), owned by the caller.  The
  *     library allocates nothing and keeps no state between calls.
@@ -69,7 +70,9 @@
  *   - Arguments are validated on the host before any HIP call, in the order:
  *     format/dtype (QR_ERR_UNSUPPORTED), counts (QR_ERR_ARG / QR_ERR_SIZE),
  *     null pointers (QR_ERR_ARG), alignment (QR_ERR_ALIGN), aliasing
- *     (QR_ERR_ALIAS).  A failed launch returns QR_ERR_HIP.
+ *     (QR_ERR_ALIAS).  A launch that the HIP runtime refuses returns
+ *     QR_ERR_HIP; the status is that of the call's own launch, so an error
+ *     left on the thread by an earlier, unrelated HIP call does not fail it.
  *   - Inputs are finite values; NaN/Inf inputs give unspecified codes.
  */
 #ifndef QR_H_
