@@ -1,0 +1,99 @@
+"""Host logic of bench.py (CPU only): algorithmic bytes, the tile sizes it
+assumes, the counter ingestion and its calibration, the kernel-source guard
+on stored traffic, and the single-GPU exit."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import workloads as W  # noqa: E402
+
+
+def test_algorithmic_bytes_of_the_bench_workload():
+    """[32 x 1024 x 4096] fp16 per rank, INT4 (1152 B per 2048 values), R = 8:
+    encode 2 + c bytes per value, reduce R*c + c + 2."""
+    w = W.WORKLOADS["int4_r8_fp16_32x1024x4096"]
+    n = 32 * 1024 * 4096
+    ab = bench.algorithmic_bytes(w)
+    assert ab["encode"] == n * 2 + n // 2048 * 1152 == 343_932_928
+    assert ab["reduce"] == 8 * (n // 2048 * 1152) + n // 2048 * 1152 + 2 * n == 947_912_704
+    assert ab["decode"] == ab["encode"]
+
+
+def test_mixed_output_format_bytes():
+    w = W.WORKLOADS["int6_r8_fp16_32x1024x4096"]      # INT4 inputs, INT8 re-encoded sum
+    tiles = w.n // 2048
+    assert bench.algorithmic_bytes(w)["reduce"] == 8 * tiles * 1152 + tiles * 2176 + 2 * w.n
+
+
+def test_tile_sizes_match_the_library_and_the_oracle():
+    import bit_quantized_all_amd as qa
+    import oracle
+
+    o = oracle.default()
+    for fmt, tb in bench.TILE_BYTES.items():
+        fid = bench.FORMAT_IDS[fmt]
+        assert qa.qr_packed_bytes(fmt, 2048) == tb == o.packed_bytes(fid, 2048), fmt
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for name, value in rows:
+            wr.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_ingest_scales_by_the_calibration_copy(tmp_path, monkeypatch):
+    """FETCH_SIZE and WRITE_SIZE are scaled so that the copy of one rank's input
+    (n * 2 bytes each way) reads as its known size; torch's own reduce kernel and
+    other kernels are ignored; medians over dispatches."""
+    wl = "int4_r8_fp16_32x1024x4096"
+    w = W.WORKLOADS[wl]
+    ab = bench.algorithmic_bytes(w)
+    kib = w.n * 2 / 1024
+    enc_r, enc_w = w.n * 2 / 1024, (ab["encode"] - w.n * 2) / 1024
+    red_r, red_w = (ab["reduce"] - ab["encode"]) / 1024, ab["encode"] / 1024
+    fetch = [("copy_kernel<...>", kib / 2), ("copy_kernel<...>", kib / 2),
+             ("void qr::encode_kernel<4, 0>(...)", enc_r / 2), ("void qr::encode_kernel<4, 0>(...)", enc_r / 2 + 1),
+             ("void qr::encode_kernel<4, 0>(...)", enc_r / 2 - 1),
+             ("void qr::reduce_kernel<4, 4, 0, 8, true>(qr::ReduceArgs)", red_r / 2),
+             ("void at::native::reduce_kernel<512, 1>(...)", 99.0), ("distribution_kernel", 5.0)]
+    write = [("copy_kernel<...>", kib), ("void qr::encode_kernel<4, 0>(...)", enc_w),
+             ("void qr::reduce_kernel<4, 4, 0, 8, true>(qr::ReduceArgs)", red_w)]
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", fetch)
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", write)
+    out_json = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_JSON", str(out_json))
+    bench.ingest_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), wl)
+    d = json.load(open(out_json))[wl]
+    assert d["fetch_scale"] == pytest.approx(2.0) and d["write_scale"] == pytest.approx(1.0)
+    assert d["bytes_per_launch"]["encode"] == pytest.approx(ab["encode"], rel=1e-9)
+    assert d["bytes_per_launch"]["reduce"] == pytest.approx(ab["reduce"], rel=1e-9)
+    assert d["kernel_source_hash"] == bench.kernel_source_hash()
+
+
+def test_stored_traffic_needs_the_same_kernel_sources(tmp_path, monkeypatch):
+    p = tmp_path / "traffic.json"
+    p.write_text(json.dumps({"wl": {"kernel_source_hash": "abc", "bytes_per_launch": {"encode": 7}}}))
+    monkeypatch.setattr(bench, "TRAFFIC_JSON", str(p))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "abc")
+    assert bench.traffic_from_profiles("encode", "wl") == 7
+    assert bench.traffic_from_profiles("reduce", "wl") is None
+    assert bench.traffic_from_profiles("encode", "other") is None
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "changed")
+    assert bench.traffic_from_profiles("encode", "wl") is None
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
