@@ -185,3 +185,24 @@ def test_too_many_tiles(L):
     assert red(L, n=n) == qr.QR_ERR_SIZE
     assert redm(L, n=n) == qr.QR_ERR_SIZE
     assert enc(L, n=2048 * ((1 << 31) - 1), x=0) == qr.QR_ERR_ARG   # largest accepted count reaches the null check
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No fallback path: with libqr.so absent every call raises instead of
+    computing anything elsewhere."""
+    import torch
+
+    from bit_quantized_all_amd import qr as Q
+
+    monkeypatch.setattr(Q, "_lib", None)
+    monkeypatch.setattr(Q, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libqr.so"))
+    Q._packed_bytes.cache_clear()
+    try:
+        with pytest.raises(RuntimeError, match="missing"):
+            Q.lib()
+        with pytest.raises(RuntimeError, match="missing"):
+            Q.qr_packed_bytes("int4", 2048)
+        with pytest.raises(RuntimeError, match="missing"):
+            Q.qr_encode("int4", torch.zeros(2048, dtype=torch.float16))
+    finally:
+        Q._packed_bytes.cache_clear()
