@@ -405,7 +405,7 @@ def main():
         g = ab[k] / (us * 1e-6) / 1e9
         kernels[k] = {"us_per_launch": round(us, 3), "launches_per_step": launches[k],
                       "algorithmic_bytes": int(ab[k]), "achieved_gbs": round(g, 1),
-                      "frac": round(g / PEAK_HBM_GBS, 4)}
+                      "frac": round(g / PEAK_HBM_GBS, 4), "traffic": traffic_from_profiles(k, name)}
     dom = max(kern_us, key=lambda k: kern_us[k] * launches[k])
     roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["achieved_gbs"],
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": kernels[dom]["frac"],
