@@ -321,45 +321,56 @@ def main():
         run()
     torch.cuda.synchronize()
 
+    # host-side markers (roctx under ROCm) around the timed regions, for traces
+    # taken with rocprofv3 --marker-trace; a no-op where torch has none
+    import contextlib
+
+    def marker(label):
+        rng = getattr(getattr(torch.cuda, "nvtx", None), "range", None)
+        return rng(label) if rng is not None else contextlib.nullcontext()
+
     # timed region 1: K clean steps between two events, rotating the buffer sets
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        run_steps[i % nsets]()
-    end.record(stream)
-    torch.cuda.synchronize()
+    with marker(f"qr.steps x{args.steps}"):
+        start.record(stream)
+        for i in range(args.steps):
+            run_steps[i % nsets]()
+        end.record(stream)
+        torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
 
     # the same K steps again, with an event between consecutive steps -> median step
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    evs[0].record(stream)
-    for i in range(args.steps):
-        run_steps[i % nsets]()
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
+    with marker(f"qr.steps_with_events x{args.steps}"):
+        evs[0].record(stream)
+        for i in range(args.steps):
+            run_steps[i % nsets]()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
     per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     ms_median = per_step[args.steps // 2] if args.steps % 2 else \
         0.5 * (per_step[args.steps // 2 - 1] + per_step[args.steps // 2])
 
     # timed region 2: each kernel alone, K steps' worth of back-to-back launches
     # between two events on the launch stream -> average launch duration
-    def timed(fn, launches):
+    def timed(label, fn, launches):
         run = runner(fn)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        e0.record(stream)
-        run()
-        e1.record(stream)
-        torch.cuda.synchronize()
+        with marker(f"qr.{label} x{launches}"):
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            torch.cuda.synchronize()
         return e0.elapsed_time(e1) / launches * 1e3
 
     kname = "reduce" if w.reduce else "decode"
     kern_us = {
-        "encode": timed(lambda: [encode(sets[i % nsets], r) for i in range(args.steps) for r in range(w.ranks)],
-                        args.steps * w.ranks),
-        kname: timed(lambda: [finish(sets[i % nsets]) for i in range(args.steps)], args.steps),
+        "encode": timed("encode", lambda: [encode(sets[i % nsets], r) for i in range(args.steps)
+                                           for r in range(w.ranks)], args.steps * w.ranks),
+        kname: timed(kname, lambda: [finish(sets[i % nsets]) for i in range(args.steps)], args.steps),
     }
     run_steps[0]()   # the outputs checked below come from one whole step on set 0
     torch.cuda.synchronize()
