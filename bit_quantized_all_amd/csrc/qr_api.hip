@@ -46,7 +46,7 @@ extern "C" {
 
 size_t qr_packed_bytes(qr_format fmt, size_t n) {
   const int tb = tile_bytes(fmt);
-  if (!tb || n % kTileValues) return 0;
+  if (!tb || n % kTileValues || too_large(n)) return 0;
   return n / kTileValues * (size_t)tb;
 }
 

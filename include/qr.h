@@ -84,7 +84,17 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* In C++ the enums below get int as their fixed underlying type, so that any
+ * int a C caller passes (an unknown format, say) is a value of the enum and
+ * the library's check can reject it without undefined behaviour; in C they
+ * are plain enums, passed as int-sized values either way. */
+#ifdef __cplusplus
+#define QR_ENUM_INT : int
+#else
+#define QR_ENUM_INT
+#endif
+
+typedef enum QR_ENUM_INT {
   QR_OK = 0,
   QR_ERR_ARG = 1,         /* null pointer, R out of [1, QR_MAX_RANKS] */
   QR_ERR_SIZE = 2,        /* n not a multiple of 2048, or more than 2^31 - 1 tiles */
@@ -97,7 +107,7 @@ typedef enum {
 /* Symmetric 32-value block formats are named by their code width, the
  * asymmetric 128-value group formats by 16 + code width, the FP4 block
  * format by 32 + code width. */
-typedef enum {
+typedef enum QR_ENUM_INT {
   QR_INT3 = 3,
   QR_INT4 = 4,
   QR_INT8 = 8,
@@ -106,14 +116,15 @@ typedef enum {
   QR_FP4 = 36
 } qr_format;
 
-typedef enum { QR_FP16 = 0, QR_BF16 = 1 } qr_dtype;
+typedef enum QR_ENUM_INT { QR_FP16 = 0, QR_BF16 = 1 } qr_dtype;
 
 #define QR_TILE_VALUES 2048
 #define QR_MAX_RANKS 16
 
 /* Bytes of the packed form of n values: n / 2048 tiles of 896 (INT3), 1152
  * (INT4 and FP4), 2176 (INT8), 1072 (ASYM4) or 2096 (ASYM8) bytes.  Returns 0
- * for an unknown format or an n that is not a multiple of 2048.  Tile sizes:
+ * for an unknown format, an n that is not a multiple of 2048, or more than
+ * 2^31 - 1 tiles (the calls' own limit).  Tile sizes:
  * "Design Highlights" (INT4 1152 B, INT3 896 B per 2048-value per-rank tile). */
 size_t qr_packed_bytes(qr_format fmt, size_t n);
 
