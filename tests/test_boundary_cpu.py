@@ -206,3 +206,22 @@ def test_missing_library_fails_loudly(monkeypatch):
             Q.qr_encode("int4", torch.zeros(2048, dtype=torch.float16))
     finally:
         Q._packed_bytes.cache_clear()
+
+
+@pytest.mark.parametrize("lang,std", [("c", "-std=c99"), ("c", "-std=c11"), ("c++", "-std=c++11"), ("c++", "-std=c++17")])
+def test_header_compiles_strictly(tmp_path, lang, std):
+    """include/qr.h is a plain C header that also compiles as C++ (pedantic,
+    warnings as errors), with the enums usable from both."""
+    import shutil
+    import subprocess
+
+    cc = "gcc" if lang == "c" else "g++"
+    if shutil.which(cc) is None:
+        pytest.skip(f"{cc} is not installed")
+    src = tmp_path / ("h.c" if lang == "c" else "h.cpp")
+    src.write_text('#include "qr.h"\n'
+                   "int main(void) { qr_format f = QR_INT4; qr_dtype d = QR_BF16; qr_status s = QR_OK;\n"
+                   "  return (int)f + (int)d + (int)s - 5 + (int)sizeof(&qr_encode) * 0; }\n")
+    r = subprocess.run([cc, std, "-pedantic", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        "-fsyntax-only", str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
