@@ -29,6 +29,10 @@ tiles):
   int4_r8_fp16_4x1024x4096  one rank's share of that reduce in the two-shot
                            scheme: R = 8 segments of n / 8 = 4 x 1024 x 4096
                            values (the same channel spread).
+  int4_r8_bf16_32x1024x4096  the [32 x 1024 x 4096] INT4 R=8 workload with bf16
+                           activations (same channel spread, its own streams).
+  int3_r2_fp16_32x1024x4096  INT3 over R=2 ranks of the same shape and spread
+                           (tensor parallelism 2, where the pages recommend INT3).
 
 Random numbers come from torch's seeded generators (Philox on the GPU, the CPU
 generator on the host); each (seed, workload, rank) gets its own stream seed.
@@ -108,6 +112,12 @@ WORKLOADS = {
                                          32 * 1024 * 4096, (32, 1024, 4096),
                                          channel_sigma=(0.01, 20.0),
                                          data_key="int4_r8_fp16_32x1024x4096"),
+    # the same shape and channel spread with bf16 activations
+    "int4_r8_bf16_32x1024x4096": Workload("int4_r8_bf16_32x1024x4096", "int4", torch.bfloat16, 8,
+                                          32 * 1024 * 4096, (32, 1024, 4096), channel_sigma=(0.01, 20.0)),
+    # INT3 over two ranks (tensor parallelism 2, where the pages recommend INT3)
+    "int3_r2_fp16_32x1024x4096": Workload("int3_r2_fp16_32x1024x4096", "int3", torch.float16, 2,
+                                          32 * 1024 * 4096, (32, 1024, 4096), channel_sigma=(0.01, 20.0)),
 }
 
 BENCH_WORKLOAD = "int4_r8_fp16_32x1024x4096"
