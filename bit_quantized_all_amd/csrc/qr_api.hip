@@ -35,8 +35,12 @@ inline bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Too many tiles for the kernels' int tile index.
-inline bool too_large(size_t n) { return n / kTileValues > (size_t)0x7fffffff; }
+// The kernels index tiles with an int and advance it by the grid stride (at
+// most kMaxGroups * kWavesPerGroup tiles) past the last tile: the tile limit
+// leaves room for that step.
+static_assert((long long)QR_MAX_TILES + (long long)kMaxGroups * kWavesPerGroup <= 0x7fffffffLL,
+              "a tile index plus one grid stride must fit in an int");
+inline bool too_large(size_t n) { return n / kTileValues > (size_t)QR_MAX_TILES; }
 
 }  // namespace qr
 
@@ -145,7 +149,7 @@ const char* qr_status_string(qr_status s) {
   switch (s) {
     case QR_OK: return "ok";
     case QR_ERR_ARG: return "invalid argument (null pointer or rank count)";
-    case QR_ERR_SIZE: return "value count is not a multiple of 2048 or exceeds 2^31 tiles";
+    case QR_ERR_SIZE: return "value count is not a multiple of 2048 or exceeds QR_MAX_TILES (2^30) tiles";
     case QR_ERR_ALIGN: return "buffer pointer is not 16-byte aligned";
     case QR_ERR_UNSUPPORTED: return "unsupported format or dtype";
     case QR_ERR_ALIAS: return "output buffer overlaps another buffer";

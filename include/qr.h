@@ -59,8 +59,8 @@
  *   decode: y = value(code) * d, exact in fp32, rounded to the I/O dtype.
  *
  * Conventions for every call:
- *   - `n` counts values and must be a multiple of 2048, of at most 2^31 - 1
- *     tiles (QR_ERR_SIZE otherwise); n == 0 is a valid empty call that
+ *   - `n` counts values and must be a multiple of 2048, of at most
+ *     QR_MAX_TILES = 2^30 tiles (QR_ERR_SIZE otherwise); n == 0 is a valid empty call that
  *     launches nothing and returns QR_OK.
  *   - Buffer pointers are DEVICE pointers (hipMalloc or the PyTorch caching
  *     allocator), 16-byte aligned (QR_ERR_ALIGN), owned by the caller.  The
@@ -97,7 +97,7 @@ extern "C" {
 typedef enum QR_ENUM_INT {
   QR_OK = 0,
   QR_ERR_ARG = 1,         /* null pointer, R out of [1, QR_MAX_RANKS] */
-  QR_ERR_SIZE = 2,        /* n not a multiple of 2048, or more than 2^31 - 1 tiles */
+  QR_ERR_SIZE = 2,        /* n not a multiple of 2048, or more than QR_MAX_TILES tiles */
   QR_ERR_ALIGN = 3,       /* a buffer pointer is not 16-byte aligned */
   QR_ERR_UNSUPPORTED = 4, /* unknown format or dtype */
   QR_ERR_ALIAS = 5,       /* an output overlaps an input or the other output */
@@ -120,11 +120,14 @@ typedef enum QR_ENUM_INT { QR_FP16 = 0, QR_BF16 = 1 } qr_dtype;
 
 #define QR_TILE_VALUES 2048
 #define QR_MAX_RANKS 16
+/* Largest tile count of a call (2^30 tiles = 2^41 values, beyond any one
+ * GPU's memory). */
+#define QR_MAX_TILES 1073741824
 
 /* Bytes of the packed form of n values: n / 2048 tiles of 896 (INT3), 1152
  * (INT4 and FP4), 2176 (INT8), 1072 (ASYM4) or 2096 (ASYM8) bytes.  Returns 0
  * for an unknown format, an n that is not a multiple of 2048, or more than
- * 2^31 - 1 tiles (the calls' own limit).  Tile sizes:
+ * QR_MAX_TILES tiles (the calls' own limit).  Tile sizes:
  * "Design Highlights" (INT4 1152 B, INT3 896 B per 2048-value per-rank tile). */
 size_t qr_packed_bytes(qr_format fmt, size_t n);
 

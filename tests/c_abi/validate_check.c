@@ -33,7 +33,7 @@ static const qr_format kFormats[6] = {QR_INT3, QR_INT4, QR_INT8, QR_ASYM4, QR_AS
 static const size_t kTile[6] = {896, 1152, 2176, 1072, 2096, 1152};
 
 static void packed_bytes(void) {
-  const size_t max_tiles = ((size_t)1 << 31) - 1;
+  const size_t max_tiles = QR_MAX_TILES;
   for (int f = 0; f < 6; ++f) {
     EXPECT(qr_packed_bytes(kFormats[f], 0), 0);
     EXPECT(qr_packed_bytes(kFormats[f], 2048), kTile[f]);
@@ -54,7 +54,7 @@ static void packed_bytes(void) {
 }
 
 static void encode_decode(void) {
-  const size_t n = 4 * 2048, huge = ((size_t)1 << 31) * 2048;
+  const size_t n = 4 * 2048, huge = ((size_t)QR_MAX_TILES + 1) * 2048;
   for (int f = 0; f < 6; ++f) {
     const qr_format fmt = kFormats[f];
     const size_t pb = 4 * kTile[f];
@@ -84,7 +84,7 @@ static void encode_decode(void) {
 }
 
 static void reduce(void) {
-  const size_t n = 2048, huge = ((size_t)1 << 31) * 2048;
+  const size_t n = 2048, huge = ((size_t)QR_MAX_TILES + 1) * 2048;
   const void *ranks[QR_MAX_RANKS + 1];
   for (int r = 0; r <= QR_MAX_RANKS; ++r) ranks[r] = CP(A + (uintptr_t)r * 0x100000);
   EXPECT(qr_reduce_compressed(QR_INT4, QR_FP16, ranks, 0, P(B), P(C), n, NULL), QR_ERR_ARG);

@@ -177,14 +177,15 @@ def test_fp4_validation(L):
 
 
 def test_too_many_tiles(L):
-    """A value count whose tile index would not fit the kernels' int is a size
-    error, before any HIP call (so fake pointers are fine)."""
-    n = 2048 * (1 << 31)
+    """More than QR_MAX_TILES = 2^30 tiles (where a tile index plus one grid
+    stride could leave the kernels' int) is a size error, before any HIP call
+    (so fake pointers are fine)."""
+    n = 2048 * ((1 << 30) + 1)
     assert enc(L, n=n) == qr.QR_ERR_SIZE
     assert dec(L, n=n) == qr.QR_ERR_SIZE
     assert red(L, n=n) == qr.QR_ERR_SIZE
     assert redm(L, n=n) == qr.QR_ERR_SIZE
-    assert enc(L, n=2048 * ((1 << 31) - 1), x=0) == qr.QR_ERR_ARG   # largest accepted count reaches the null check
+    assert enc(L, n=2048 * (1 << 30), x=0) == qr.QR_ERR_ARG   # largest accepted count reaches the null check
 
 
 def test_missing_library_fails_loudly(monkeypatch):
