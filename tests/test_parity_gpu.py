@@ -848,6 +848,62 @@ def test_calls_on_a_side_stream(qa, oracle):
     assert np.array_equal(u16(y), wy) and np.array_equal(u16(yd), wy)
 
 
+def test_concurrent_host_threads(qa, oracle):
+    """The library keeps no state between calls: four host threads, each with
+    its own stream (default priority) and format, run encode -> reduce ->
+    decode 20 times at once (ctypes releases the GIL around each call, so the
+    C calls overlap).  Every thread's result matches the oracle."""
+    import threading
+
+    n, R, iters = 37 * 2048, 3, 20
+    cases = [("int3", "fp16"), ("int4", "bf16"), ("int8", "fp16"), ("fp4", "bf16")]
+    bufs = []
+    for k, (fmt, dt) in enumerate(cases):
+        xs = [gen("outliers", dt, n, seed=200 + 10 * k + r) for r in range(R)]
+        pb = qa.qr_packed_bytes(fmt, n)
+        bufs.append({
+            "host": xs,
+            "x": [dev(x, DT[dt]) for x in xs],
+            "packed": [torch.empty(pb, dtype=torch.uint8, device="cuda") for _ in range(R)],
+            "out": torch.empty(pb, dtype=torch.uint8, device="cuda"),
+            "y": torch.empty(n, dtype=DT[dt], device="cuda"),
+            "yd": torch.empty(n, dtype=DT[dt], device="cuda"),
+            "stream": torch.cuda.Stream(),
+        })
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(k):
+        fmt, dt = cases[k]
+        b = bufs[k]
+        try:
+            for _ in range(iters):
+                for x, p in zip(b["x"], b["packed"]):
+                    qa.qr_encode(fmt, x, p, stream=b["stream"])
+                qa.qr_reduce_compressed(fmt, DT[dt], b["packed"], n, packed_out=b["out"], y_out=b["y"],
+                                        stream=b["stream"])
+                qa.qr_decode(fmt, b["out"], n, DT[dt], y=b["yd"], stream=b["stream"])
+        except Exception as e:   # reported by the main thread
+            errors.append((fmt, e))
+
+    log("concurrent host threads")
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for b in bufs:
+        b["stream"].synchronize()
+    assert not errors, errors
+    for (fmt, dt), b in zip(cases, bufs):
+        wr = [oracle.encode(BITS[fmt], dt, x) for x in b["host"]]
+        wout, wy = oracle.reduce(BITS[fmt], dt, wr, n)
+        for p, w in zip(b["packed"], wr):
+            assert np.array_equal(p.cpu().numpy(), w), fmt
+        assert np.array_equal(b["out"].cpu().numpy(), wout), fmt
+        assert np.array_equal(u16(b["y"]), wy) and np.array_equal(u16(b["yd"]), wy), fmt
+
+
 @pytest.mark.parametrize("fmt", FMTS + AFMTS + ("fp4",))
 def test_repeat_runs_are_bit_identical(qa, fmt):
     """Determinism control: the same inputs through every entry point twice,
