@@ -67,6 +67,20 @@ def traffic_from_profiles(kernel, workload):
     return d.get("bytes_per_launch", {}).get(kernel)
 
 
+MAX_SETS = 1024
+
+
+def buffer_sets(w, pb, rotate_mib):
+    """Number of identical buffer sets to rotate through: enough that each
+    kernel's reads over one pass of the sets add up to rotate_mib MiB (the
+    encodes read the R inputs of a set, the reduce its R packed buffers, the
+    decode its one packed buffer), at most MAX_SETS.  A launch's inputs were
+    then last read that many bytes of traffic ago, beyond what the 256 MB
+    last-level cache holds."""
+    reads = min(w.ranks * 2 * w.n, (w.ranks if w.reduce else 1) * pb)
+    return max(1, min(MAX_SETS, -(-(rotate_mib << 20) // reads)))
+
+
 KERNEL_KEYS = {"encode": "encode_kernel", "reduce": "reduce_kernel", "decode": "decode_kernel"}
 COPY_KEY = "copy_kernel"   # torch's device copy kernel (the calibration copy of --copy-ref)
 
@@ -232,8 +246,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-mib", type=int, default=512,
                     help="rotate through enough identical buffer sets (inputs, packed, outputs) that "
-                         "one pass over them touches at least this many MiB, so that the 256 MB "
-                         "last-level cache cannot hold the working set (at most 64 sets)")
+                         "every kernel reads at least this many MiB over one pass of the sets, so "
+                         "that the 256 MB last-level cache cannot serve a launch's reads from an "
+                         f"earlier launch (at most {MAX_SETS} sets)")
     ap.add_argument("--graph", action="store_true",
                     help="capture the timed launches in HIP graphs and replay them (removes the "
                          "host-side launch cost that bounds small messages)")
@@ -274,7 +289,7 @@ def main():
     pb = qa.qr_packed_bytes(w.fmt, w.n)
     pbo = qa.qr_packed_bytes(w.out_fmt, w.n)
     set_bytes = w.ranks * (2 * w.n + pb) + (pbo if w.reduce else 0) + 2 * w.n
-    nsets = max(1, min(64, -(-(args.rotate_mib << 20) // set_bytes)))
+    nsets = buffer_sets(w, pb, args.rotate_mib)
 
     class BufferSet:
         def __init__(self, xs):

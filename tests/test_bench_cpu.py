@@ -97,3 +97,24 @@ def test_more_than_one_gpu_exits_with_a_message():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_buffer_sets_cover_every_kernels_reads():
+    """The rotation is sized by the smallest per-kernel read footprint of a set,
+    so that no kernel re-reads its inputs from the last-level cache."""
+    import workloads as W
+    mib = 1 << 20
+    wb = W.WORKLOADS["int4_r8_fp16_32x1024x4096"]          # reduce reads 8 x 72 MiB per set
+    assert bench.buffer_sets(wb, 1152 * wb.n // 2048, 512) == 1
+    wc = W.WORKLOADS["int4_fp16_codec_32x1024x4096"]       # decode reads 72 MiB per set
+    assert bench.buffer_sets(wc, 1152 * wc.n // 2048, 512) == 8
+    w3 = W.WORKLOADS["int3_r8_bf16_1024x8192"]             # reduce reads 8 x 3.5 MiB per set
+    assert bench.buffer_sets(w3, 896 * w3.n // 2048, 512) == 19
+    w2 = W.WORKLOADS["int3_bf16_codec_8m"]                 # decode reads 3.5 MiB per set
+    assert bench.buffer_sets(w2, 896 * w2.n // 2048, 512) == 147
+    tiny = W.small(wb, 2048)                               # capped
+    assert bench.buffer_sets(tiny, 1152, 512) == bench.MAX_SETS
+    for w, pb in ((wc, 1152 * wc.n // 2048), (w3, 896 * w3.n // 2048), (w2, 896 * w2.n // 2048)):
+        n = bench.buffer_sets(w, pb, 512)
+        reads = min(w.ranks * 2 * w.n, (w.ranks if w.reduce else 1) * pb)
+        assert n * reads >= 512 * mib > (n - 1) * reads

@@ -13,6 +13,10 @@ def test_catalogue():
     assert w["int3_r8_bf16_1024x8192"].n == 1024 * 8192 and w["int3_r8_bf16_1024x8192"].ranks == 8
     assert w["int4_r8_fp16_32x1024x4096"].n == 134217728
     assert w["sweep_r4_fp16_int8_512mib"].n == 268435456
+    # the codec workload's input is rank 0's input of the INT4 R=8 workload
+    c, b = W.small(w["int4_fp16_codec_32x1024x4096"], 4096 * 4), W.small(w["int4_r8_fp16_32x1024x4096"], 4096 * 4)
+    assert not c.reduce and c.ranks == 1
+    assert torch.equal(W.rank_input(c, 0, seed=1).view(torch.int16), W.rank_input(b, 0, seed=1).view(torch.int16))
     for v in w.values():
         assert v.n % 2048 == 0
 

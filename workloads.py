@@ -33,6 +33,9 @@ tiles):
                            activations (same channel spread, its own streams).
   int3_r2_fp16_32x1024x4096  INT3 over R=2 ranks of the same shape and spread
                            (tensor parallelism 2, where the pages recommend INT3).
+  int4_fp16_codec_32x1024x4096  encode + decode only of rank 0's input of the
+                           [32 x 1024 x 4096] INT4 workload (the receive side's
+                           decode of gathered tiles, at full size).
 
 Random numbers come from torch's seeded generators (Philox on the GPU, the CPU
 generator on the host); each (seed, workload, rank) gets its own stream seed.
@@ -118,6 +121,11 @@ WORKLOADS = {
     # INT3 over two ranks (tensor parallelism 2, where the pages recommend INT3)
     "int3_r2_fp16_32x1024x4096": Workload("int3_r2_fp16_32x1024x4096", "int3", torch.float16, 2,
                                           32 * 1024 * 4096, (32, 1024, 4096), channel_sigma=(0.01, 20.0)),
+    # encode + decode only, on rank 0's input of the INT4 R=8 workload
+    "int4_fp16_codec_32x1024x4096": Workload("int4_fp16_codec_32x1024x4096", "int4", torch.float16, 1,
+                                             32 * 1024 * 4096, (32, 1024, 4096),
+                                             channel_sigma=(0.01, 20.0), reduce=False,
+                                             data_key="int4_r8_fp16_32x1024x4096"),
 }
 
 BENCH_WORKLOAD = "int4_r8_fp16_32x1024x4096"
