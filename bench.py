@@ -31,14 +31,29 @@ METRIC = "GB/s of FP16 input through encode+compressed-reduce+decode; % HBM peak
 PEAK_HBM_GBS = 8000.0
 TILE_BYTES = {"int3": 896, "int4": 1152, "int8": 2176, "asym4": 1072, "asym8": 2096, "fp4": 1152}
 FORMAT_IDS = {"int3": 3, "int4": 4, "int8": 8, "asym4": 20, "asym8": 24, "fp4": 36}
-KERNEL_SOURCES = ["bit_quantized_all_amd/csrc/qr_kernels.hpp", "bit_quantized_all_amd/csrc/qr_codec.hpp"]
+KERNEL_SOURCE_DIR = "bit_quantized_all_amd/csrc"
+
+
+def kernel_sources():
+    """Every source file the library is built from (relative paths, sorted),
+    with the C ABI header."""
+    d = os.path.join(ROOT, KERNEL_SOURCE_DIR)
+    return sorted(os.path.join(KERNEL_SOURCE_DIR, f) for f in os.listdir(d)) + ["include/qr.h"]
 
 
 def kernel_source_hash():
+    """Hash of the library as built: every source file and the compiler flags
+    and per-unit definitions of bit_quantized_all_amd/build.py.  Stored counter
+    results apply only to a build with the same hash."""
+    from bit_quantized_all_amd import build as hip_build
+
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in kernel_sources():
+        h.update(p.encode())
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
+    h.update(repr(hip_build.FLAGS).encode())
+    h.update(repr([(os.path.basename(src), defs) for src, defs in hip_build.SOURCES]).encode())
     return h.hexdigest()[:16]
 
 
@@ -70,15 +85,31 @@ def traffic_from_profiles(kernel, workload):
 MAX_SETS = 1024
 
 
-def buffer_sets(w, pb, rotate_mib):
+def set_traffic(w, pb, pbo=None):
+    """Smallest per-kernel read and write footprint of one buffer set: the
+    encodes read the R inputs of a set and write its R packed buffers, the
+    reduce reads the R packed buffers and writes the re-encoded sum and y,
+    the decode reads one packed buffer and writes y."""
+    pbo = pb if pbo is None else pbo
+    if w.reduce:
+        reads = min(w.ranks * 2 * w.n, w.ranks * pb)
+        writes = min(w.ranks * pb, pbo + 2 * w.n)
+    else:
+        reads = min(2 * w.n, pb)
+        writes = min(pb, 2 * w.n)
+    return reads, writes
+
+
+def buffer_sets(w, pb, rotate_mib, pbo=None):
     """Number of identical buffer sets to rotate through: enough that each
-    kernel's reads over one pass of the sets add up to rotate_mib MiB (the
-    encodes read the R inputs of a set, the reduce its R packed buffers, the
-    decode its one packed buffer), at most MAX_SETS.  A launch's inputs were
-    then last read that many bytes of traffic ago, beyond what the 256 MB
-    last-level cache holds."""
-    reads = min(w.ranks * 2 * w.n, (w.ranks if w.reduce else 1) * pb)
-    return max(1, min(MAX_SETS, -(-(rotate_mib << 20) // reads)))
+    kernel's reads, and its writes, over one pass of the sets add up to
+    rotate_mib MiB, at most MAX_SETS.  A launch's inputs were then last read,
+    and its outputs last written, that many bytes of the kernel's own traffic
+    ago, beyond what the 256 MB last-level cache holds: no launch reads its
+    inputs from the cache, and no output still dirty in the cache is written
+    again (which would spare its HBM write)."""
+    reads, writes = set_traffic(w, pb, pbo)
+    return max(1, min(MAX_SETS, -(-(rotate_mib << 20) // min(reads, writes))))
 
 
 KERNEL_KEYS = {"encode": "encode_kernel", "reduce": "reduce_kernel", "decode": "decode_kernel"}
@@ -246,9 +277,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-mib", type=int, default=512,
                     help="rotate through enough identical buffer sets (inputs, packed, outputs) that "
-                         "every kernel reads at least this many MiB over one pass of the sets, so "
-                         "that the 256 MB last-level cache cannot serve a launch's reads from an "
-                         f"earlier launch (at most {MAX_SETS} sets)")
+                         "every kernel reads, and writes, at least this many MiB over one pass of "
+                         "the sets, so that the 256 MB last-level cache can neither serve a launch's "
+                         "reads nor absorb its writes from an earlier launch "
+                         f"(at most {MAX_SETS} sets)")
     ap.add_argument("--graph", action="store_true",
                     help="capture the timed launches in HIP graphs and replay them (removes the "
                          "host-side launch cost that bounds small messages)")
@@ -289,7 +321,7 @@ def main():
     pb = qa.qr_packed_bytes(w.fmt, w.n)
     pbo = qa.qr_packed_bytes(w.out_fmt, w.n)
     set_bytes = w.ranks * (2 * w.n + pb) + (pbo if w.reduce else 0) + 2 * w.n
-    nsets = buffer_sets(w, pb, args.rotate_mib)
+    nsets = buffer_sets(w, pb, args.rotate_mib, pbo)
 
     class BufferSet:
         def __init__(self, xs):

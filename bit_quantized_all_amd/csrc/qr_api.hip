@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "qr.h"
 #include "qr_kernels.hpp"
 
@@ -41,6 +43,21 @@ inline bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 static_assert((long long)QR_MAX_TILES + (long long)kMaxGroups * kWavesPerGroup <= 0x7fffffffLL,
               "a tile index plus one grid stride must fit in an int");
 inline bool too_large(size_t n) { return n / kTileValues > (size_t)QR_MAX_TILES; }
+
+int device_compute_units() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];  // 0 = not yet queried
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+  if (dev < kMaxDevices) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 }  // namespace qr
 

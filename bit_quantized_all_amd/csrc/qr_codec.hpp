@@ -280,12 +280,17 @@ __device__ __forceinline__ void pack_int3_pair(const uint32_t* c, uint32_t& low,
 // one block: encode (from exact dtype values in fp32) and decode
 // ---------------------------------------------------------------------------
 
-// Magic constant 2^23 + Q: adding it to a value in [-Q, Q) rounds that value
-// to an integer (half to even, since Q is even) and leaves the biased code in
-// the low mantissa bits: bits(2^23 + Q + k) = 0x4B000000 + (k + Q).
+// Magic constant 2^23 + 0x6400 + Q: adding it to a value in [-Q, Q) rounds
+// that value to an integer (half to even: the sum lies in [2^23, 2^24), where
+// the fp32 spacing is 1) and leaves the biased code q = k + Q in the low byte
+// of the mantissa, with 0x64 in the byte above it:
+// bits(2^23 + 0x6400 + Q + k) = 0x4B006400 + q.  The low two bytes are then
+// the fp16 pattern of 1024 + q, so one byte permute makes an fp16 pair of
+// codes (used by the fused decode of the re-encoded sum).
+constexpr float kMagicBase = 8388608.0f + 25600.0f;  // 2^23 + 0x6400
 template <int BITS>
 __device__ __forceinline__ constexpr float magic() {
-  return 8388608.0f + Format<BITS>::kQ;
+  return kMagicBase + Format<BITS>::kQ;
 }
 
 // fp32(1 / d), correctly rounded, for d a positive finite fp16 value: the
@@ -312,12 +317,12 @@ __device__ __forceinline__ uint32_t block_scale(float m, float& d, float& e) {
 }
 
 // Code of one value: q = clamp(rint(RN32(x * e)), -Q, Q-1) + Q, returned as
-// the bits of 2^23 + q (low byte = q).  Clamping after the magic add equals
-// clamping before rounding because the bounds are integers.
+// the bits of 2^23 + 0x6400 + q (low byte = q).  Clamping after the magic add
+// equals clamping before rounding because the bounds are integers.
 template <int BITS>
 __device__ __forceinline__ uint32_t quantize(float v) {
   constexpr int Q = Format<BITS>::kQ;
-  const float t = __builtin_amdgcn_fmed3f(v + magic<BITS>(), 8388608.0f, 8388608.0f + (2 * Q - 1));
+  const float t = __builtin_amdgcn_fmed3f(v + magic<BITS>(), kMagicBase, kMagicBase + (2 * Q - 1));
   return __builtin_bit_cast(uint32_t, t);
 }
 
@@ -325,6 +330,19 @@ __device__ __forceinline__ uint32_t quantize(float v) {
 template <int BITS>
 __device__ __forceinline__ float code_value(uint32_t t) {
   return __builtin_bit_cast(float, t) - magic<BITS>();
+}
+
+// fp16 pair dtype_RNE((q0 - Q) * d), dtype_RNE((q1 - Q) * d) from two
+// quantize() results and the fp16 scale d: one byte permute gives the fp16
+// pair (1024 + q0, 1024 + q1), one packed subtract the exact codes q - Q, and
+// one packed multiply the products, each rounded once to fp16 (the exact
+// product has at most 8 + 11 significant bits, so this equals rounding the
+// exact fp32 product, overflow to infinity included).
+template <int BITS>
+__device__ __forceinline__ uint32_t decode_pair_fp16(uint32_t t0, uint32_t t1, f16x2 d2) {
+  constexpr _Float16 kBias = (_Float16)(-(1024 + Format<BITS>::kQ));
+  const f16x2 k = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(t1, t0, 0x05040100u)) + f16x2{kBias, kBias};
+  return __builtin_bit_cast(uint32_t, k * d2);
 }
 
 // Packs 32 codes (low byte of each t[i]) into the lane's block.
@@ -665,22 +683,66 @@ __device__ __forceinline__ void decode_block_asym(const Block<F>& blk, uint32_t 
 // global <-> lane block data
 // ---------------------------------------------------------------------------
 
-// Global loads and stores with an optional non-temporal hint (for data that
-// is streamed through once and should not displace other cache lines).
-template <bool NT, typename T>
-__device__ __forceinline__ T ld(const T* p) {
-  if constexpr (NT)
-    return __builtin_nontemporal_load(p);
-  else
-    return *p;
+// Every global access of the kernels goes through a buffer resource that
+// covers one tile: its base address is wave-uniform (scalar registers, one
+// scalar add per tile), lanes add a 32-bit byte offset that stays the same
+// from tile to tile, and an access past the tile's bytes reads 0 and writes
+// nothing.  POL is the cache-policy operand (see cache_policy()).
+struct TileRef {
+  __amdgpu_buffer_rsrc_t r;
+};
+
+// Dword 3 of a buffer resource on gfx9 parts: 32-bit data format, the rest 0.
+constexpr int kBufferResourceDword3 = 0x00020000;
+
+__device__ __forceinline__ TileRef tile_ref(const void* base, uint32_t bytes) {
+  return {__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferResourceDword3)};
 }
 
-template <bool NT, typename T>
-__device__ __forceinline__ void st(T v, T* p) {
-  if constexpr (NT)
-    __builtin_nontemporal_store(v, p);
-  else
-    *p = v;
+// Cache-policy operand of the memory instructions: 0 = default (cached,
+// write-back), kNT = non-temporal (streamed through once).  Other values are
+// the raw operand (bit 0 and bit 4 set the coherence scope of a store).
+constexpr int kNT = 2;
+template <int POL>
+constexpr int cache_policy() {
+  return POL;
+}
+
+template <int NT>
+__device__ __forceinline__ u32x4 ld16(TileRef t, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(t.r, (int)off, 0, cache_policy<NT>());
+}
+template <int NT>
+__device__ __forceinline__ u32x2 ld8(TileRef t, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(t.r, (int)off, 0, cache_policy<NT>());
+}
+template <int NT>
+__device__ __forceinline__ uint32_t ld4(TileRef t, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(t.r, (int)off, 0, cache_policy<NT>());
+}
+template <int NT>
+__device__ __forceinline__ uint32_t ld2(TileRef t, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(t.r, (int)off, 0, cache_policy<NT>());
+}
+template <int NT>
+__device__ __forceinline__ void st16(TileRef t, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, t.r, (int)off, 0, cache_policy<NT>());
+}
+template <int NT>
+__device__ __forceinline__ void st8(TileRef t, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, t.r, (int)off, 0, cache_policy<NT>());
+}
+template <int NT>
+__device__ __forceinline__ void st4(TileRef t, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, t.r, (int)off, 0, cache_policy<NT>());
+}
+template <int NT>
+__device__ __forceinline__ void st2(TileRef t, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, t.r, (int)off, 0, cache_policy<NT>());
+}
+template <int NT>
+__device__ __forceinline__ void st1(TileRef t, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, t.r, (int)off, 0, cache_policy<NT>());
 }
 
 // ---------------------------------------------------------------------------
@@ -700,7 +762,7 @@ __device__ __forceinline__ int swz8(int c) { return c ^ ((c >> 1) & 15); }
 
 // Row-order chunks (held in blk.w[0..3] = chunk l, blk.w[4..7] = chunk 64 + l)
 // to the lane's own block (its 32 code bytes in order).  tl: 128 chunks.
-__device__ __forceinline__ void stage_codes_in(u32x4* tl, int lane, CodeBlock<8>& blk) {
+__device__ __forceinline__ void stage_codes_in(u32x4* tl, uint32_t lane, CodeBlock<8>& blk) {
   tl[swz8(lane)] = u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]};
   tl[swz8(64 + lane)] = u32x4{blk.w[4], blk.w[5], blk.w[6], blk.w[7]};
   wave_lds_sync();
@@ -712,46 +774,44 @@ __device__ __forceinline__ void stage_codes_in(u32x4* tl, int lane, CodeBlock<8>
 
 // The lane's block to row-order chunks, stored coalesced at tile + 16 * lane
 // and tile + 1024 + 16 * lane.
-template <bool NT>
-__device__ __forceinline__ void stage_codes_out(u32x4* tl, int lane, const CodeBlock<8>& blk,
-                                                uint8_t* __restrict__ tile) {
+template <int NT>
+__device__ __forceinline__ void stage_codes_out(u32x4* tl, uint32_t lane, const CodeBlock<8>& blk, TileRef tile) {
   tl[swz8(2 * lane)] = u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]};
   tl[swz8(2 * lane + 1)] = u32x4{blk.w[4], blk.w[5], blk.w[6], blk.w[7]};
   wave_lds_sync();
   const u32x4 a = tl[swz8(lane)], b = tl[swz8(64 + lane)];
   wave_lds_sync();
-  st<NT>(a, reinterpret_cast<u32x4*>(tile) + lane);
-  st<NT>(b, reinterpret_cast<u32x4*>(tile) + 64 + lane);
+  st16<NT>(tile, 16 * lane, a);
+  st16<NT>(tile, 1024 + 16 * lane, b);
 }
 
 // Codes of block g and its scale.  For the asymmetric formats `scale`
 // receives one dword of the tile's 48-byte scale / zero-point region (dword
 // min(g & 15, 11)), and group_meta() later hands every lane its group's
 // values: one memory instruction instead of a 2-byte and a 1-byte load.
-template <int F, bool NT>
-__device__ __forceinline__ void load_block(const uint8_t* __restrict__ tile, int g, Block<F>& blk,
-                                           uint32_t& scale) {
+template <int F, int NT>
+__device__ __forceinline__ void load_block(TileRef tile, uint32_t g, Block<F>& blk, uint32_t& scale) {
   constexpr int BITS = Format<F>::kCodeBits;
   if constexpr (BITS == 4) {
-    const u32x4 v = ld<NT>(reinterpret_cast<const u32x4*>(tile + 16 * g));
+    const u32x4 v = ld16<NT>(tile, 16 * g);
     blk.w[0] = v.x; blk.w[1] = v.y; blk.w[2] = v.z; blk.w[3] = v.w;
   } else if constexpr (BITS == 8) {
     // row-order chunks g and 64 + g; stage_codes_in() turns them into block g
-    const u32x4 a = ld<NT>(reinterpret_cast<const u32x4*>(tile) + g);
-    const u32x4 b = ld<NT>(reinterpret_cast<const u32x4*>(tile) + 64 + g);
+    const u32x4 a = ld16<NT>(tile, 16 * g);
+    const u32x4 b = ld16<NT>(tile, 1024 + 16 * g);
     blk.w[0] = a.x; blk.w[1] = a.y; blk.w[2] = a.z; blk.w[3] = a.w;
     blk.w[4] = b.x; blk.w[5] = b.y; blk.w[6] = b.z; blk.w[7] = b.w;
   } else {
-    const u32x2 lw = ld<NT>(reinterpret_cast<const u32x2*>(tile + 8 * g));
+    const u32x2 lw = ld8<NT>(tile, 8 * g);
     blk.low[0] = lw.x; blk.low[1] = lw.y;
-    blk.high = ld<NT>(reinterpret_cast<const uint32_t*>(tile + Format<3>::kHighOffset + 4 * g));
+    blk.high = ld4<NT>(tile, Format<3>::kHighOffset + 4 * g);
   }
   if constexpr (Format<F>::kAsym) {
     static_assert(Format<F>::kZeroOffset == Format<F>::kScaleOffset + 32, "scales then zero points");
-    const int j = (g & 15) < 11 ? (g & 15) : 11;
-    scale = ld<NT>(reinterpret_cast<const uint32_t*>(tile + Format<F>::kScaleOffset + 4 * j));
+    const uint32_t j = (g & 15) < 11 ? (g & 15) : 11;
+    scale = ld4<NT>(tile, Format<F>::kScaleOffset + 4 * j);
   } else {
-    scale = ld<NT>(reinterpret_cast<const uint16_t*>(tile + Format<F>::kScaleOffset + 2 * g));
+    scale = ld2<NT>(tile, Format<F>::kScaleOffset + 2 * g);
   }
 }
 
@@ -769,26 +829,25 @@ __device__ __forceinline__ uint32_t group_meta(uint32_t m, int g) {
 // Stores block g; for the asymmetric formats the first lane of each group
 // stores the group's scale and zero point (scale bits | zero point << 16).
 // 8-bit codes are stored by stage_codes_out(), only their scale here.
-template <int F, bool NT>
-__device__ __forceinline__ void store_block(uint8_t* __restrict__ tile, int g, const Block<F>& blk,
-                                            uint32_t scale) {
+template <int F, int NT>
+__device__ __forceinline__ void store_block(TileRef tile, uint32_t g, const Block<F>& blk, uint32_t scale) {
   constexpr int BITS = Format<F>::kCodeBits;
   if constexpr (BITS == 4) {
-    st<NT>(u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]}, reinterpret_cast<u32x4*>(tile + 16 * g));
+    st16<NT>(tile, 16 * g, u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]});
   } else if constexpr (BITS == 8) {
     // the codes go through stage_codes_out(); only the scale is stored here
   } else {
-    st<NT>(u32x2{blk.low[0], blk.low[1]}, reinterpret_cast<u32x2*>(tile + 8 * g));
-    st<NT>(blk.high, reinterpret_cast<uint32_t*>(tile + Format<3>::kHighOffset + 4 * g));
+    st8<NT>(tile, 8 * g, u32x2{blk.low[0], blk.low[1]});
+    st4<NT>(tile, Format<3>::kHighOffset + 4 * g, blk.high);
   }
   if constexpr (Format<F>::kAsym) {
     if ((g & 3) == 0) {
-      const int grp = g >> 2;
-      st<NT>((uint16_t)scale, reinterpret_cast<uint16_t*>(tile + Format<F>::kScaleOffset + 2 * grp));
-      st<NT>((uint8_t)(scale >> 16), tile + Format<F>::kZeroOffset + grp);
+      const uint32_t grp = g >> 2;
+      st2<NT>(tile, Format<F>::kScaleOffset + 2 * grp, scale);
+      st1<NT>(tile, Format<F>::kZeroOffset + grp, scale >> 16);
     }
   } else {
-    st<NT>((uint16_t)scale, reinterpret_cast<uint16_t*>(tile + Format<F>::kScaleOffset + 2 * g));
+    st2<NT>(tile, Format<F>::kScaleOffset + 2 * g, scale);
   }
 }
 

@@ -53,6 +53,30 @@ namespace qr {
 #ifndef QR_RED_NT_STORE
 #define QR_RED_NT_STORE 1
 #endif
+// Cache-policy operands (cache_policy()) of the memory instructions, per
+// kernel and direction; the reduce's y output has its own.
+#define QR_POL(nt) ((nt) ? kNT : 0)
+#ifndef QR_ENC_LOAD_POL
+#define QR_ENC_LOAD_POL QR_POL(QR_ENC_NT_LOAD)
+#endif
+#ifndef QR_ENC_STORE_POL
+#define QR_ENC_STORE_POL QR_POL(QR_ENC_NT_STORE)
+#endif
+#ifndef QR_DEC_LOAD_POL
+#define QR_DEC_LOAD_POL QR_POL(QR_DEC_NT_LOAD)
+#endif
+#ifndef QR_DEC_STORE_POL
+#define QR_DEC_STORE_POL QR_POL(QR_DEC_NT_STORE)
+#endif
+#ifndef QR_RED_LOAD_POL
+#define QR_RED_LOAD_POL QR_POL(QR_RED_NT_LOAD)
+#endif
+#ifndef QR_RED_STORE_POL
+#define QR_RED_STORE_POL QR_POL(QR_RED_NT_STORE)
+#endif
+#ifndef QR_RED_Y_STORE_POL
+#define QR_RED_Y_STORE_POL QR_RED_STORE_POL
+#endif
 // Tiles each encode wave processes (the next one prefetched while encoding).
 #ifndef QR_ENC_TILES_PER_WAVE
 #define QR_ENC_TILES_PER_WAVE 1
@@ -66,6 +90,28 @@ namespace qr {
 #ifndef QR_RED_LOADS_FIRST_REGS
 #define QR_RED_LOADS_FIRST_REGS 128
 #endif
+// 1: the fused decode of the re-encoded sum builds fp16 outputs as packed
+// fp16 pairs (byte permute, packed subtract, packed multiply).
+#ifndef QR_Y_HALF_PAIRS
+#define QR_Y_HALF_PAIRS 1
+#endif
+// 1: reduce waves loop over tiles with the next tile's loads in flight
+// (grid of QR_RED_GROUPS_PER_CU workgroups per CU); 0: one tile per wave.
+// Measured slower and kept off: INT3 R = 2, 134M fp16 values per rank,
+// 74.8 -> 88.2 us (4 workgroups per CU) and 87.2 us (6); INT4 R = 8
+// 150.9 -> 172.6 us; the second register set also halves the occupancy.
+#ifndef QR_RED_PREFETCH
+#define QR_RED_PREFETCH 0
+#endif
+#ifndef QR_RED_GROUPS_PER_CU
+#define QR_RED_GROUPS_PER_CU 4
+#endif
+// 1: the reduce decodes its ranks in load order (each rank's codes pass an
+// empty asm that depends on the previous rank's sum), so rank r's decode
+// waits only for the loads of ranks 0..r.
+#ifndef QR_RED_RANK_ORDER
+#define QR_RED_RANK_ORDER 1
+#endif
 // Encode workgroups resident on one CU at a time.  Every encode wave has its
 // whole 4 KB input tile in flight at once; a full CU (8 workgroups, 32 waves)
 // keeps more requests outstanding than HBM serves best, and 5 workgroups
@@ -75,14 +121,36 @@ namespace qr {
 #ifndef QR_ENC_GROUPS_PER_CU
 #define QR_ENC_GROUPS_PER_CU 5
 #endif
+// Reduce workgroups resident on one CU at a time (0: as many as registers
+// allow), set the same way.  The fused reduce writes more than it reads
+// (y alone is 2 bytes per value); with fewer waves in flight HBM serves its
+// mix of reads and writes better: INT3 R = 2, 134M fp16 values per rank,
+// 74.9 -> 72.2 us at 5 workgroups (20 waves), 72.6 us at 6; INT3 R = 4 at
+// 512 MiB per rank 189.5 -> 182.3 us.  Kernels whose registers already allow
+// at most 20 waves per CU (INT4 R = 8: 16) are not affected.
+#ifndef QR_RED_GROUPS_PER_CU_MAX
+#define QR_RED_GROUPS_PER_CU_MAX 5
+#endif
+// Decode workgroups resident on one CU at a time (0: no limit).
+#ifndef QR_DEC_GROUPS_PER_CU_MAX
+#define QR_DEC_GROUPS_PER_CU_MAX 0
+#endif
 constexpr int kWavesPerGroup = QR_WAVES_PER_GROUP;
 constexpr int kThreads = kWave * kWavesPerGroup;
 constexpr int kMaxGroups = QR_MAX_GROUPS;
 constexpr int kLdsBytesPerCU = 160 * 1024;
-// 16-byte LDS chunks per encode wave: the tile's kChunks, plus the unused
-// rest of the 1 / QR_ENC_GROUPS_PER_CU share of the CU's LDS
-constexpr int kEncLdsChunks = kLdsBytesPerCU / QR_ENC_GROUPS_PER_CU / (16 * kWavesPerGroup);
-static_assert(kEncLdsChunks >= kChunks, "the encode tile must fit in its LDS share");
+
+// 16-byte LDS chunks per wave for a kernel that needs `needed` of them and
+// may have at most `groups` workgroups on one CU (0: no limit): the whole
+// 1 / groups share of the CU's LDS when that is more than it needs, so that
+// no further workgroup fits.
+constexpr int lds_chunks(int needed, int groups) {
+  return groups > 0 && kLdsBytesPerCU / groups / (16 * kWavesPerGroup) > needed
+             ? kLdsBytesPerCU / groups / (16 * kWavesPerGroup)
+             : needed;
+}
+constexpr int kEncLdsChunks = lds_chunks(kChunks, QR_ENC_GROUPS_PER_CU);
+constexpr int kDecLdsChunks = lds_chunks(kChunks, QR_DEC_GROUPS_PER_CU_MAX);
 
 // ---------------------------------------------------------------------------
 // encode
@@ -92,7 +160,7 @@ template <int BITS, int DT>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restrict__ x,
                                                           uint8_t* __restrict__ packed, int ntiles) {
   __shared__ u32x4 lds[kWavesPerGroup][kEncLdsChunks];
-  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
   u32x4* tl = lds[wave];
   const int stride = gridDim.x * kWavesPerGroup;
@@ -101,9 +169,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restr
   // the next tile's 4 KB is loaded into registers while this one is encoded
   u32x4 v[4];
   auto load_tile = [&](int t) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)t * (kTileValues * 2));
+    const TileRef src = tile_ref(x + (size_t)t * (kTileValues * 2), kTileValues * 2);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = ld<QR_ENC_NT_LOAD>(src + lane + kWave * k);
+    for (int k = 0; k < 4; ++k) v[k] = ld16<QR_ENC_LOAD_POL>(src, 16 * (lane + kWave * k));
   };
   load_tile(tile);
   for (; tile < ntiles; tile += stride) {
@@ -130,9 +198,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restr
         scale = quantize_words<BITS, DT>(w, t);
       pack_block<BITS>(t, blk);
     }
-    uint8_t* tp = packed + (size_t)tile * Format<BITS>::kTileBytes;
-    if constexpr (kStaged<BITS>) stage_codes_out<QR_ENC_NT_STORE>(tl, lane, blk, tp);
-    store_block<BITS, QR_ENC_NT_STORE>(tp, lane, blk, scale);
+    const TileRef tp = tile_ref(packed + (size_t)tile * Format<BITS>::kTileBytes, Format<BITS>::kTileBytes);
+    if constexpr (kStaged<BITS>) stage_codes_out<QR_ENC_STORE_POL>(tl, lane, blk, tp);
+    store_block<BITS, QR_ENC_STORE_POL>(tp, lane, blk, scale);
   }
 }
 
@@ -140,40 +208,42 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restr
 // decode
 // ---------------------------------------------------------------------------
 
-// One lane's 32 output values (block order) into the wave's LDS tile.
-template <int DT>
-__device__ __forceinline__ void write_lane_values(u32x4* tl, int lane, const float (&y)[kBlockValues]) {
+// One lane's 32 output values (block order, as 16 packed dtype pairs) into
+// the wave's LDS tile.
+__device__ __forceinline__ void write_lane_words(u32x4* tl, uint32_t lane, const uint32_t (&w)[kBlockValues / 2]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    u32x4 c;
-    c.x = pack2<DT>(y[8 * j + 0], y[8 * j + 1]);
-    c.y = pack2<DT>(y[8 * j + 2], y[8 * j + 3]);
-    c.z = pack2<DT>(y[8 * j + 4], y[8 * j + 5]);
-    c.w = pack2<DT>(y[8 * j + 6], y[8 * j + 7]);
-    tl[swz(4 * lane + j)] = c;
-  }
+  for (int j = 0; j < 4; ++j) tl[swz(4 * lane + j)] = u32x4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+}
+
+// The same from 32 fp32 values, each rounded to the dtype (nearest even).
+template <int DT>
+__device__ __forceinline__ void write_lane_values(u32x4* tl, uint32_t lane, const float (&y)[kBlockValues]) {
+  uint32_t w[kBlockValues / 2];
+#pragma unroll
+  for (int i = 0; i < kBlockValues / 2; ++i) w[i] = pack2<DT>(y[2 * i], y[2 * i + 1]);
+  write_lane_words(tl, lane, w);
 }
 
 // The wave's LDS tile to global memory in row order (coalesced 16-byte stores).
-template <bool NT>
-__device__ __forceinline__ void flush_tile(u32x4* tl, int lane, uint8_t* __restrict__ dst) {
+template <int NT>
+__device__ __forceinline__ void flush_tile(u32x4* tl, uint32_t lane, TileRef dst) {
   wave_lds_sync();
-  u32x4* out = reinterpret_cast<u32x4*>(dst);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) st<NT>(tl[swz(lane + kWave * k)], out + lane + kWave * k);
+  for (int k = 0; k < 4; ++k) st16<NT>(dst, 16 * (lane + kWave * k), tl[swz(lane + kWave * k)]);
   wave_lds_sync();
 }
 
 template <int BITS, int DT>
 __global__ __launch_bounds__(kThreads) void decode_kernel(const uint8_t* __restrict__ packed,
                                                           uint8_t* __restrict__ y, int ntiles) {
-  __shared__ u32x4 lds[kWavesPerGroup][kChunks];
-  const int lane = threadIdx.x & (kWave - 1);
+  __shared__ u32x4 lds[kWavesPerGroup][kDecLdsChunks];
+  const uint32_t lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
   for (int tile = blockIdx.x * kWavesPerGroup + wave; tile < ntiles; tile += gridDim.x * kWavesPerGroup) {
     Block<BITS> blk;
     uint32_t scale;
-    load_block<BITS, QR_DEC_NT_LOAD>(packed + (size_t)tile * Format<BITS>::kTileBytes, lane, blk, scale);
+    load_block<BITS, QR_DEC_LOAD_POL>(tile_ref(packed + (size_t)tile * Format<BITS>::kTileBytes, Format<BITS>::kTileBytes),
+                                     lane, blk, scale);
     if constexpr (kStaged<BITS>) stage_codes_in(lds[wave], lane, blk);
     float kk[kBlockValues];
     float dd, ddo;  // scales of even and odd values
@@ -194,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint8_t* __restr
 #pragma unroll
     for (int i = 0; i < kBlockValues; ++i) v[i] = kk[i] * ((i & 1) ? ddo : dd);
     write_lane_values<DT>(lds[wave], lane, v);
-    flush_tile<QR_DEC_NT_STORE>(lds[wave], lane, y + (size_t)tile * (kTileValues * 2));
+    flush_tile<QR_DEC_STORE_POL>(lds[wave], lane, tile_ref(y + (size_t)tile * (kTileValues * 2), kTileValues * 2));
   }
 }
 
@@ -210,152 +280,226 @@ struct ReduceArgs {
   int ntiles;
 };
 
+// LDS chunks per reduce wave: the fp16/bf16 output tile (WITH_Y) and / or the
+// 2 KB staging region of 8-bit codes, which reuses the output tile's space.
+template <int BI, int BO, bool WITH_Y>
+constexpr int kReduceLdsChunks =
+    lds_chunks(WITH_Y ? kChunks : ((kStaged<BI> || kStaged<BO>) ? kChunks / 2 : 1), QR_RED_GROUPS_PER_CU_MAX);
+
+// Every rank's block `lane` of tile `tile` (codes and scale) into registers.
+template <int BI, int R>
+__device__ __forceinline__ void load_ranks(const ReduceArgs& a, int tile, uint32_t lane, Block<BI> (&blk)[R],
+                                           uint32_t (&sc)[R]) {
+  const size_t toff = (size_t)tile * Format<BI>::kTileBytes;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    load_block<BI, QR_RED_LOAD_POL>(tile_ref(a.ranks[r] + toff, Format<BI>::kTileBytes), lane, blk[r], sc[r]);
+}
+
+// Passes a block's registers through an empty asm that also reads `after`:
+// code that uses the block is then scheduled after `after` is computed.
+template <int CB>
+__device__ __forceinline__ void order_after(CodeBlock<CB>& blk, uint32_t& sc, float after) {
+  if constexpr (CB == 3) {
+    asm volatile("" : "+v"(blk.low[0]), "+v"(blk.low[1]), "+v"(blk.high), "+v"(sc) : "v"(after));
+  } else if constexpr (CB == 4) {
+    asm volatile("" : "+v"(blk.w[0]), "+v"(blk.w[1]), "+v"(blk.w[2]), "+v"(blk.w[3]), "+v"(sc) : "v"(after));
+  } else {
+    asm volatile("" : "+v"(blk.w[0]), "+v"(blk.w[1]), "+v"(blk.w[2]), "+v"(blk.w[3]), "+v"(blk.w[4]),
+                 "+v"(blk.w[5]), "+v"(blk.w[6]), "+v"(blk.w[7]), "+v"(sc) : "v"(after));
+  }
+}
+
+// The reduction of one tile whose R blocks are in registers: exact decode,
+// fp32 rank-order sum, re-encode into packed_out and (WITH_Y) decode into y.
+template <int BI, int BO, int DT, int R, bool WITH_Y>
+__device__ __forceinline__ void reduce_tile(const ReduceArgs& a, int tile, uint32_t lane, u32x4* tl,
+                                            Block<BI> (&blk)[R], uint32_t (&sc)[R]) {
+  constexpr int TBO = Format<BO>::kTileBytes;   // re-encoded tiles
+  constexpr float kInvShift = 1.0f / (1 << Format<BI>::kShift);
+  // exact decode of every rank, fp32 sum in rank order: s = y_0, s = s + y_r
+  float s[kBlockValues];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    // rank r's codes enter its decode only after rank r - 1 is summed, so the
+    // decodes run in load order and each waits only for its own loads
+    if constexpr (QR_RED_RANK_ORDER)
+      if (r > 0) order_after(blk[r], sc[r], s[kBlockValues - 1]);
+    if constexpr (kStaged<BI>) stage_codes_in(tl, lane, blk[r]);
+    float kk[kBlockValues];
+    float dd, ddo;  // scales of even and odd values (exact products with kk)
+    if constexpr (Format<BI>::kAsym) {
+      sc[r] = group_meta(sc[r], lane);
+      decode_block_asym<BI>(blk[r], sc[r] >> 16, kk);
+      dd = scale_f32(sc[r]);
+      ddo = dd * (1.0f / (1 << Format<BI>::kOddShift));
+    } else if constexpr (Format<BI>::kFp4) {
+      decode_block_fp4(blk[r], kk);
+      dd = ddo = scale_f32(sc[r]);
+    } else {
+      decode_block<BI>(blk[r], kk);
+      dd = scale_f32(sc[r]) * kInvShift;
+      ddo = dd;
+    }
+    if (r == 0) {
+      // fma(k, d, +0) is the exact product k * d up to the sign of a zero
+      // (+0 for -0); it lets the fp16 halves of the asymmetric decode feed
+      // one mixed-precision FMA.  Asymmetric inputs reduce only into an
+      // asymmetric format, whose code of +-0 is z either way, so no later
+      // step can observe the difference.
+#pragma unroll
+      for (int i = 0; i < kBlockValues; ++i) {
+        if constexpr (Format<BI>::kAsym)
+          s[i] = __builtin_fmaf(kk[i], (i & 1) ? ddo : dd, 0.0f);
+        else
+          s[i] = kk[i] * dd;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kBlockValues; ++i) s[i] = __builtin_fmaf(kk[i], (i & 1) ? ddo : dd, s[i]);
+    }
+  }
+  // re-encode dtype_RNE(s): rounding is monotonic and symmetric, so the
+  // block maximum (group range) of the rounded values is the rounded
+  // maximum of |s| (range of s)
+  uint32_t scale;
+  Block<BO> ob;
+  uint32_t yw[kBlockValues / 2];  // decoded re-encoded sum as dtype pairs (WITH_Y)
+  if constexpr (Format<BO>::kAsym) {
+    // range ends from integer maxima of the fp32 patterns (as in quantize_words_asym)
+    int hb = 0;
+    uint32_t lb = 0;
+#pragma unroll
+    for (int i = 0; i < kBlockValues; ++i) {
+      hb = __builtin_elementwise_max(hb, __builtin_bit_cast(int, s[i]));
+      lb = __builtin_elementwise_max(lb, __builtin_bit_cast(uint32_t, s[i]));
+    }
+    hb = group_max_i32(hb);
+    lb = group_max_u32(lb);
+    const float hi = round_to_dtype<DT>(__builtin_bit_cast(float, hb));
+    const float lo = (lb & 0x80000000u) ? round_to_dtype<DT>(__builtin_bit_cast(float, lb)) : 0.0f;
+    float d, e, z;
+    scale = group_params<BO>(lo, hi, d, e, z);
+    const float zb = z - 256.0f;
+    uint32_t t[kBlockValues];
+#pragma unroll
+    for (int i = 0; i < kBlockValues; i += 2) {
+      float v0, v1;
+      round_scale2<DT>(s[i], s[i + 1], e, v0, v1);
+      t[i] = quantize_asym<BO>(v0, zb);
+      t[i + 1] = quantize_asym<BO>(v1, zb);
+    }
+    if constexpr (WITH_Y) {  // decode of the re-encoded sum, straight from the codes
+      const float zm = 8388608.0f + z;
+#pragma unroll
+      for (int i = 0; i < kBlockValues; i += 2)
+        yw[i / 2] = pack2<DT>(code_value_asym(t[i], zm) * d, code_value_asym(t[i + 1], zm) * d);
+    }
+    pack_block<BO>(t, ob);
+  } else if constexpr (Format<BO>::kFp4) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kBlockValues; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(s[i]));
+    float d, e;
+    scale = fp4_block_scale(round_to_dtype<DT>(m), d, e);
+    float v[kBlockValues];
+#pragma unroll
+    for (int i = 0; i < kBlockValues; i += 2) round_scale2<DT>(s[i], s[i + 1], e, v[i], v[i + 1]);
+    pack_block_fp4(v, ob);
+    if constexpr (WITH_Y) {  // decode of the re-encoded sum from its codes
+      float kk[kBlockValues];
+      decode_block_fp4(ob, kk);
+#pragma unroll
+      for (int i = 0; i < kBlockValues; i += 2) yw[i / 2] = pack2<DT>(kk[i] * d, kk[i + 1] * d);
+    }
+  } else {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kBlockValues; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(s[i]));
+    float d, e;
+    scale = block_scale<BO>(round_to_dtype<DT>(m), d, e);
+    uint32_t t[kBlockValues];
+#pragma unroll
+    for (int i = 0; i < kBlockValues; i += 2) {
+      float v0, v1;
+      round_scale2<DT>(s[i], s[i + 1], e, v0, v1);
+      t[i] = quantize<BO>(v0);
+      t[i + 1] = quantize<BO>(v1);
+    }
+    if constexpr (WITH_Y) {  // decode of the re-encoded sum, straight from the codes
+      if constexpr (DT == kFp16 && QR_Y_HALF_PAIRS) {
+        const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)scale);
+#pragma unroll
+        for (int i = 0; i < kBlockValues; i += 2) yw[i / 2] = decode_pair_fp16<BO>(t[i], t[i + 1], f16x2{dh, dh});
+      } else {
+#pragma unroll
+        for (int i = 0; i < kBlockValues; i += 2)
+          yw[i / 2] = pack2<DT>(code_value<BO>(t[i]) * d, code_value<BO>(t[i + 1]) * d);
+      }
+    }
+    pack_block<BO>(t, ob);
+  }
+  const TileRef otile = tile_ref(a.out + (size_t)tile * TBO, TBO);
+  if constexpr (kStaged<BO>) {
+    // codes through the LDS staging region first, then the output tile
+    stage_codes_out<QR_RED_STORE_POL>(tl, lane, ob, otile);
+    store_block<BO, QR_RED_STORE_POL>(otile, lane, ob, scale);
+    if constexpr (WITH_Y) write_lane_words(tl, lane, yw);
+  } else {
+    if constexpr (WITH_Y) write_lane_words(tl, lane, yw);
+    store_block<BO, QR_RED_STORE_POL>(otile, lane, ob, scale);
+  }
+  if constexpr (WITH_Y)
+    flush_tile<QR_RED_Y_STORE_POL>(tl, lane, tile_ref(a.y + (size_t)tile * (kTileValues * 2), kTileValues * 2));
+}
+
+// Whether every rank's loads are issued before the decode starts: where R
+// blocks of codes fit in registers beside the sum and the decode temporaries
+// (with 8-bit codes at R = 15 and 16 they would not: the compiler then parks
+// registers in AGPRs and the kernel drops to one wave per SIMD).
+template <int BI, int R>
+constexpr bool kLoadsFirst = QR_RED_LOADS_FIRST && R * (int)(sizeof(Block<BI>) / 4 + 1) <= QR_RED_LOADS_FIRST_REGS;
+
 template <int BI, int BO, int DT, int R, bool WITH_Y>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
   static_assert(Format<BI>::kAsym == Format<BO>::kAsym && Format<BI>::kFp4 == Format<BO>::kFp4,
                 "a reduce stays within one format family");
-  // per wave: the fp16/bf16 output tile (WITH_Y) and / or the 2 KB staging
-  // region of 8-bit codes, which reuses the output tile's space
-  constexpr int kLdsChunks = WITH_Y ? kChunks : ((kStaged<BI> || kStaged<BO>) ? kChunks / 2 : 1);
-  __shared__ u32x4 lds[kWavesPerGroup][kLdsChunks];
-  constexpr int TB = Format<BI>::kTileBytes;    // input tiles
-  constexpr int TBO = Format<BO>::kTileBytes;   // re-encoded tiles
-  constexpr float kInvShift = 1.0f / (1 << Format<BI>::kShift);
-  const int lane = threadIdx.x & (kWave - 1);
+  __shared__ u32x4 lds[kWavesPerGroup][kReduceLdsChunks<BI, BO, WITH_Y>];
+  const uint32_t lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
-  for (int tile = blockIdx.x * kWavesPerGroup + wave; tile < a.ntiles; tile += gridDim.x * kWavesPerGroup) {
-    const size_t toff = (size_t)tile * TB;
-    Block<BI> blk[R];
-    uint32_t sc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) load_block<BI, QR_RED_NT_LOAD>(a.ranks[r] + toff, lane, blk[r], sc[r]);
-    // every rank's loads in flight before decoding starts, where R blocks of
-    // codes fit in registers beside the sum and the decode temporaries (with
-    // 8-bit codes at R = 15 and 16 they would not: the compiler then parks
-    // registers in AGPRs and the kernel drops to one wave per SIMD)
-    if constexpr (QR_RED_LOADS_FIRST && R * (int)(sizeof(Block<BI>) / 4 + 1) <= QR_RED_LOADS_FIRST_REGS)
+  const int stride = gridDim.x * kWavesPerGroup;
+  int tile = blockIdx.x * kWavesPerGroup + wave;
+  if constexpr (QR_RED_PREFETCH) {
+    // Each wave loops over several tiles with two register sets: the next
+    // tile's loads are in flight while the current tile is reduced.
+    if (tile >= a.ntiles) return;
+    Block<BI> ba[R], bb[R];
+    uint32_t sa[R], sb[R];
+    load_ranks<BI, R>(a, tile, lane, ba, sa);
+    for (;;) {
+      int next = tile + stride;
+      const bool more = next < a.ntiles;
+      if (more) load_ranks<BI, R>(a, next, lane, bb, sb);
       __builtin_amdgcn_sched_barrier(0);
-    // exact decode of every rank, fp32 sum in rank order: s = y_0, s = s + y_r
-    float s[kBlockValues];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if constexpr (kStaged<BI>) stage_codes_in(lds[wave], lane, blk[r]);
-      float kk[kBlockValues];
-      float dd, ddo;  // scales of even and odd values (exact products with kk)
-      if constexpr (Format<BI>::kAsym) {
-        sc[r] = group_meta(sc[r], lane);
-        decode_block_asym<BI>(blk[r], sc[r] >> 16, kk);
-        dd = scale_f32(sc[r]);
-        ddo = dd * (1.0f / (1 << Format<BI>::kOddShift));
-      } else if constexpr (Format<BI>::kFp4) {
-        decode_block_fp4(blk[r], kk);
-        dd = ddo = scale_f32(sc[r]);
-      } else {
-        decode_block<BI>(blk[r], kk);
-        dd = scale_f32(sc[r]) * kInvShift;
-        ddo = dd;
-      }
-      if (r == 0) {
-        // fma(k, d, +0) is the exact product k * d up to the sign of a zero
-        // (+0 for -0); it lets the fp16 halves of the asymmetric decode feed
-        // one mixed-precision FMA.  Asymmetric inputs reduce only into an
-        // asymmetric format, whose code of +-0 is z either way, so no later
-        // step can observe the difference.
-#pragma unroll
-        for (int i = 0; i < kBlockValues; ++i) {
-          if constexpr (Format<BI>::kAsym)
-            s[i] = __builtin_fmaf(kk[i], (i & 1) ? ddo : dd, 0.0f);
-          else
-            s[i] = kk[i] * dd;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < kBlockValues; ++i) s[i] = __builtin_fmaf(kk[i], (i & 1) ? ddo : dd, s[i]);
-      }
+      reduce_tile<BI, BO, DT, R, WITH_Y>(a, tile, lane, lds[wave], ba, sa);
+      if (!more) break;
+      tile = next;
+      next = tile + stride;
+      const bool more2 = next < a.ntiles;
+      if (more2) load_ranks<BI, R>(a, next, lane, ba, sa);
+      __builtin_amdgcn_sched_barrier(0);
+      reduce_tile<BI, BO, DT, R, WITH_Y>(a, tile, lane, lds[wave], bb, sb);
+      if (!more2) break;
+      tile = next;
     }
-    // re-encode dtype_RNE(s): rounding is monotonic and symmetric, so the
-    // block maximum (group range) of the rounded values is the rounded
-    // maximum of |s| (range of s)
-    uint32_t scale;
-    Block<BO> ob;
-    float yv[kBlockValues];  // decoded re-encoded sum (WITH_Y)
-    if constexpr (Format<BO>::kAsym) {
-      // range ends from integer maxima of the fp32 patterns (as in quantize_words_asym)
-      int hb = 0;
-      uint32_t lb = 0;
-#pragma unroll
-      for (int i = 0; i < kBlockValues; ++i) {
-        hb = __builtin_elementwise_max(hb, __builtin_bit_cast(int, s[i]));
-        lb = __builtin_elementwise_max(lb, __builtin_bit_cast(uint32_t, s[i]));
-      }
-      hb = group_max_i32(hb);
-      lb = group_max_u32(lb);
-      const float hi = round_to_dtype<DT>(__builtin_bit_cast(float, hb));
-      const float lo = (lb & 0x80000000u) ? round_to_dtype<DT>(__builtin_bit_cast(float, lb)) : 0.0f;
-      float d, e, z;
-      scale = group_params<BO>(lo, hi, d, e, z);
-      const float zb = z - 256.0f;
-      uint32_t t[kBlockValues];
-#pragma unroll
-      for (int i = 0; i < kBlockValues; i += 2) {
-        float v0, v1;
-        round_scale2<DT>(s[i], s[i + 1], e, v0, v1);
-        t[i] = quantize_asym<BO>(v0, zb);
-        t[i + 1] = quantize_asym<BO>(v1, zb);
-      }
-      if constexpr (WITH_Y) {  // decode of the re-encoded sum, straight from the codes
-        const float zm = 8388608.0f + z;
-#pragma unroll
-        for (int i = 0; i < kBlockValues; ++i) yv[i] = code_value_asym(t[i], zm) * d;
-      }
-      pack_block<BO>(t, ob);
-    } else if constexpr (Format<BO>::kFp4) {
-      float m = 0.0f;
-#pragma unroll
-      for (int i = 0; i < kBlockValues; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(s[i]));
-      float d, e;
-      scale = fp4_block_scale(round_to_dtype<DT>(m), d, e);
-      float v[kBlockValues];
-#pragma unroll
-      for (int i = 0; i < kBlockValues; i += 2) round_scale2<DT>(s[i], s[i + 1], e, v[i], v[i + 1]);
-      pack_block_fp4(v, ob);
-      if constexpr (WITH_Y) {  // decode of the re-encoded sum from its codes
-        float kk[kBlockValues];
-        decode_block_fp4(ob, kk);
-#pragma unroll
-        for (int i = 0; i < kBlockValues; ++i) yv[i] = kk[i] * d;
-      }
-    } else {
-      float m = 0.0f;
-#pragma unroll
-      for (int i = 0; i < kBlockValues; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(s[i]));
-      float d, e;
-      scale = block_scale<BO>(round_to_dtype<DT>(m), d, e);
-      uint32_t t[kBlockValues];
-#pragma unroll
-      for (int i = 0; i < kBlockValues; i += 2) {
-        float v0, v1;
-        round_scale2<DT>(s[i], s[i + 1], e, v0, v1);
-        t[i] = quantize<BO>(v0);
-        t[i + 1] = quantize<BO>(v1);
-      }
-      if constexpr (WITH_Y) {  // decode of the re-encoded sum, straight from the codes
-#pragma unroll
-        for (int i = 0; i < kBlockValues; ++i) yv[i] = code_value<BO>(t[i]) * d;
-      }
-      pack_block<BO>(t, ob);
+  } else {
+    for (; tile < a.ntiles; tile += stride) {
+      Block<BI> blk[R];
+      uint32_t sc[R];
+      load_ranks<BI, R>(a, tile, lane, blk, sc);
+      if constexpr (kLoadsFirst<BI, R>) __builtin_amdgcn_sched_barrier(0);
+      reduce_tile<BI, BO, DT, R, WITH_Y>(a, tile, lane, lds[wave], blk, sc);
     }
-    uint8_t* otile = a.out + (size_t)tile * TBO;
-    if constexpr (kStaged<BO>) {
-      // codes through the LDS staging region first, then the output tile
-      stage_codes_out<QR_RED_NT_STORE>(lds[wave], lane, ob, otile);
-      store_block<BO, QR_RED_NT_STORE>(otile, lane, ob, scale);
-      if constexpr (WITH_Y) write_lane_values<DT>(lds[wave], lane, yv);
-    } else {
-      if constexpr (WITH_Y) write_lane_values<DT>(lds[wave], lane, yv);
-      store_block<BO, QR_RED_NT_STORE>(otile, lane, ob, scale);
-    }
-    if constexpr (WITH_Y) flush_tile<QR_RED_NT_STORE>(lds[wave], lane, a.y + (size_t)tile * (kTileValues * 2));
   }
 }
 
@@ -423,9 +567,23 @@ qr_status launch_reduce_dt(const ReduceArgs& a, dim3 grid, hipStream_t st) {
   }
 }
 
+// Compute units of the current device (qr_api.hip; 0 if it cannot be queried).
+int device_compute_units();
+
+// Reduce grid: one wave per tile, or with QR_RED_PREFETCH at most
+// QR_RED_GROUPS_PER_CU workgroups per compute unit, each wave looping.
+inline dim3 reduce_grid(size_t ntiles) {
+  dim3 g = grid_for(ntiles);
+  if constexpr (QR_RED_PREFETCH) {
+    const int cus = device_compute_units();
+    if (cus > 0 && g.x > (unsigned)(cus * QR_RED_GROUPS_PER_CU)) g.x = (unsigned)(cus * QR_RED_GROUPS_PER_CU);
+  }
+  return g;
+}
+
 template <int BI, int BO>
 qr_status launch_reduce(int dt, const ReduceArgs& a, hipStream_t st) {
-  const dim3 grid = grid_for((size_t)a.ntiles);
+  const dim3 grid = reduce_grid((size_t)a.ntiles);
   return dt == kFp16 ? launch_reduce_dt<BI, BO, kFp16>(a, grid, st) : launch_reduce_dt<BI, BO, kBf16>(a, grid, st);
 }
 

@@ -99,22 +99,48 @@ def test_more_than_one_gpu_exits_with_a_message():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
-def test_buffer_sets_cover_every_kernels_reads():
-    """The rotation is sized by the smallest per-kernel read footprint of a set,
-    so that no kernel re-reads its inputs from the last-level cache."""
+def test_buffer_sets_cover_every_kernels_reads_and_writes():
+    """The rotation is sized by the smallest per-kernel read or write footprint
+    of a set, so that no kernel re-reads its inputs from the last-level cache
+    and no kernel re-writes an output that may still be dirty there."""
     import workloads as W
     mib = 1 << 20
-    wb = W.WORKLOADS["int4_r8_fp16_32x1024x4096"]          # reduce reads 8 x 72 MiB per set
-    assert bench.buffer_sets(wb, 1152 * wb.n // 2048, 512) == 1
-    wc = W.WORKLOADS["int4_fp16_codec_32x1024x4096"]       # decode reads 72 MiB per set
+    wb = W.WORKLOADS["int4_r8_fp16_32x1024x4096"]          # reduce writes 72 + 256 MiB per set
+    assert bench.buffer_sets(wb, 1152 * wb.n // 2048, 512) == 2
+    wc = W.WORKLOADS["int4_fp16_codec_32x1024x4096"]       # decode reads, encode writes 72 MiB per set
     assert bench.buffer_sets(wc, 1152 * wc.n // 2048, 512) == 8
-    w3 = W.WORKLOADS["int3_r8_bf16_1024x8192"]             # reduce reads 8 x 3.5 MiB per set
-    assert bench.buffer_sets(w3, 896 * w3.n // 2048, 512) == 19
+    w3 = W.WORKLOADS["int3_r8_bf16_1024x8192"]             # reduce writes 3.5 + 16 MiB per set
+    assert bench.buffer_sets(w3, 896 * w3.n // 2048, 512) == 27
     w2 = W.WORKLOADS["int3_bf16_codec_8m"]                 # decode reads 3.5 MiB per set
     assert bench.buffer_sets(w2, 896 * w2.n // 2048, 512) == 147
+    w6 = W.WORKLOADS["int6_r8_fp16_32x1024x4096"]          # INT8 re-encoded sum: 136 + 256 MiB
+    assert bench.buffer_sets(w6, 1152 * w6.n // 2048, 512, 2176 * w6.n // 2048) == 2
     tiny = W.small(wb, 2048)                               # capped
     assert bench.buffer_sets(tiny, 1152, 512) == bench.MAX_SETS
-    for w, pb in ((wc, 1152 * wc.n // 2048), (w3, 896 * w3.n // 2048), (w2, 896 * w2.n // 2048)):
+    for w, pb in ((wb, 1152 * wb.n // 2048), (wc, 1152 * wc.n // 2048), (w3, 896 * w3.n // 2048),
+                  (w2, 896 * w2.n // 2048)):
         n = bench.buffer_sets(w, pb, 512)
-        reads = min(w.ranks * 2 * w.n, (w.ranks if w.reduce else 1) * pb)
-        assert n * reads >= 512 * mib > (n - 1) * reads
+        if w.reduce:
+            reads = min(w.ranks * 2 * w.n, w.ranks * pb)
+            writes = min(w.ranks * pb, pb + 2 * w.n)
+        else:
+            reads = writes = min(2 * w.n, pb)
+        least = min(reads, writes)
+        assert n * least >= 512 * mib > (n - 1) * least
+
+
+def test_kernel_source_hash_covers_every_source_and_the_build_flags(monkeypatch):
+    """Stored counter traffic is keyed to the build: any library source file,
+    the compiler flags or a per-unit definition changes the key."""
+    from bit_quantized_all_amd import build as hip_build
+    srcs = bench.kernel_sources()
+    csrc = os.path.join(ROOT, "bit_quantized_all_amd", "csrc")
+    assert set(os.path.join("bit_quantized_all_amd", "csrc", f) for f in os.listdir(csrc)) <= set(srcs)
+    assert "include/qr.h" in srcs
+    base = bench.kernel_source_hash()
+    monkeypatch.setattr(hip_build, "FLAGS", hip_build.FLAGS + ["-DQR_RED_GROUPS_PER_CU_MAX=3"])
+    assert bench.kernel_source_hash() != base
+    monkeypatch.undo()
+    assert bench.kernel_source_hash() == base
+    monkeypatch.setattr(hip_build, "SOURCES", hip_build.SOURCES[:-1])
+    assert bench.kernel_source_hash() != base
