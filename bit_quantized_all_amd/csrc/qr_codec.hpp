@@ -56,6 +56,13 @@ enum { kFp16 = 0, kBf16 = 1 };
 // (FP4 E2M1 codes in 32-value blocks).
 template <int F>
 struct Format;
+// 1: INT3 codes decode through a byte table (one permute maps four 3-bit
+// codes to the FP8 E4M3 values of code - 4, one conversion turns two of them
+// into fp32); 0: through signed bytes 32 * (code - 4).
+#ifndef QR_INT3_TABLE_DECODE
+#define QR_INT3_TABLE_DECODE 1
+#endif
+
 template <>
 struct Format<3> {
   static constexpr bool kAsym = false;
@@ -65,7 +72,7 @@ struct Format<3> {
   static constexpr int kTileBytes = 896;   // 512 (2-bit plane) + 256 (1-bit plane) + 128
   static constexpr int kScaleOffset = 768;
   static constexpr int kHighOffset = 512;  // the 1-bit plane
-  static constexpr int kShift = 5;         // decoded bytes hold 32 * k
+  static constexpr int kShift = QR_INT3_TABLE_DECODE ? 0 : 5;  // decoded values are 2^kShift * k
 };
 template <>
 struct Format<4> {
@@ -210,18 +217,31 @@ __device__ __forceinline__ void round_scale2(float s0, float s1, float e, float&
   }
 }
 
+// A 32-bit constant held in a VGPR, so that a three-operand bit operation can
+// take it together with a second constant (one scalar operand per VOP3).
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+  asm("" : "+v"(c));
+  return c;
+}
+
 // Signed byte i of x as fp32 (one SDWA conversion on gfx950).
 __device__ __forceinline__ float sbyte(uint32_t x, int i) { return (float)(int8_t)(x >> (8 * i)); }
 
 // ---------------------------------------------------------------------------
-// wave-private LDS tile: 256 chunks of 16 bytes.  Chunk c lives in slot
-// c ^ t(c), an XOR swizzle of its low three bits by bits 2..5 chosen so that
-// both the row-order access (lane L, chunk L + 64k) and the block-order access
-// (lane l, chunks 4l + j) hit distinct 16-byte bank groups within every 8 and
-// every 16 consecutive lanes (no bank conflicts for 32- or 64-bank LDS).
+// wave-private LDS tile: 256 chunks of 16 bytes, stored with one 16-byte pad
+// after every 16 chunks (272 slots): chunk c lives in slot c + c / 16.  Both
+// access orders are then a per-lane base plus a constant (the instruction's
+// immediate offset, so the addresses are computed once per wave):
+//   row order   (lane L, chunks L + 64k): slot L + L / 16 + 68k
+//   block order (lane l, chunks 4l + j):  slot 4l + l / 4 + j
+// and the 16 lanes of every aligned group of 16 hit 16 distinct slots modulo
+// 16 (distinct 16-byte bank groups of a 64-bank LDS) in both orders.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ int swz(int c) { return c ^ (((c >> 2) & 5) | (((c >> 2) ^ (c >> 4)) & 2)); }
+constexpr int kTileSlots = kChunks + kChunks / 16;
+
+__device__ __forceinline__ uint32_t row_slot(uint32_t lane, int k) { return lane + (lane >> 4) + 68 * k; }
+__device__ __forceinline__ uint32_t block_slot(uint32_t lane, int j) { return 4 * lane + (lane >> 2) + j; }
 
 // Makes one lane's LDS writes visible to the other lanes of its wave.
 __device__ __forceinline__ void wave_lds_sync() {
@@ -437,6 +457,31 @@ __device__ __forceinline__ void decode_block(const Block<F>& blk, float (&kk)[kB
 #pragma unroll
       for (int i = 0; i < 4; ++i) kk[4 * w + i] = sbyte(a, i);
     }
+  } else if constexpr (QR_INT3_TABLE_DECODE) {
+    // Values 8u + j (u = unit 0..3) are decoded together for each j: two byte
+    // gathers give, per unit, the low-pair byte that holds value j; byte u of
+    // the 1-bit plane word holds unit u's high bits.  Byte u of `sel` is the
+    // code of value 8u + j (low pair | high bit << 2), a permute selector
+    // into the table of the FP8 E4M3 bytes of code - 4, and each conversion
+    // turns two table bytes into fp32 (exact: the values are -4 .. 3).
+    const uint32_t p03 = __builtin_amdgcn_perm(blk.low[1], blk.low[0], 0x06040200u);  // j = 0..3
+    const uint32_t p47 = __builtin_amdgcn_perm(blk.low[1], blk.low[0], 0x07050301u);  // j = 4..7
+    const uint32_t table_hi = vgpr_const(0x44403800u);  // codes 7..4: 3, 2, 1, 0
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t p = j < 4 ? p03 : p47;
+      const int i = j & 3;  // the low pair sits at bits 2i..2i+1 of each byte
+      const uint32_t lo = i ? p >> (2 * i) : p;
+      const uint32_t hi = j < 2 ? blk.high << (2 - j) : blk.high >> (j - 2);
+      const uint32_t sel = (lo & 0x03030303u) | (hi & 0x04040404u);
+      const uint32_t t = __builtin_amdgcn_perm(table_hi, 0xB8C0C4C8u, sel);  // codes 3..0: -1 .. -4
+      const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(t, 1.0f, false);
+      const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(t, 1.0f, true);
+      kk[j] = a.x;
+      kk[8 + j] = a.y;
+      kk[16 + j] = b.x;
+      kk[24 + j] = b.y;
+    }
   } else {
     // Values 8u + j (u = unit 0..3) are decoded together for each j: byte u
     // of the 1-bit plane word holds unit u's high bits, so one shift puts all
@@ -629,13 +674,6 @@ __device__ __forceinline__ uint32_t quantize_words_asym(const uint32_t (&w)[kBlo
   return params;
 }
 
-// A 32-bit constant held in a VGPR, so that a three-operand bit operation can
-// take it together with a second constant (one scalar operand per VOP3).
-__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
-  asm("" : "+v"(c));
-  return c;
-}
-
 // Decodes one block of an asymmetric format into kk[i] = (q_i - z) * 2^(kOddShift
 // * (i & 1)), exactly; odd values then take the scale s * 2^-kOddShift.
 // The fp16 pattern 0x6400 | c is the value 1024 + c (c < 1024), so one
@@ -750,23 +788,24 @@ __device__ __forceinline__ void st1(TileRef t, uint32_t off, uint32_t v) {
 // or storing it directly would make every 16-byte access of the wave stride by
 // 32 bytes.  Instead the wave moves row-order 16-byte chunks (lane l: chunks
 // l and 64 + l, coalesced) and exchanges them through a wave-private 2 KB LDS
-// region (lane l: chunks 2l and 2l + 1).  Chunk c sits in slot
-// c ^ ((c >> 1) & 15), which keeps both access orders free of bank conflicts
-// within every 8 and every 16 consecutive lanes.
+// region (lane l: chunks 2l and 2l + 1), padded like the tile: chunk c sits in
+// slot c + c / 16, so lane l's row-order slots are l + l / 16 (+ 68) and its
+// block-order slots 2l + l / 8 (+ 1), distinct modulo 16 within every 16 lanes.
 // ---------------------------------------------------------------------------
 
 template <int F>
 constexpr bool kStaged = Format<F>::kCodeBits == 8;
 
-__device__ __forceinline__ int swz8(int c) { return c ^ ((c >> 1) & 15); }
+constexpr int kStageSlots = kChunks / 2 + kChunks / 32;
 
 // Row-order chunks (held in blk.w[0..3] = chunk l, blk.w[4..7] = chunk 64 + l)
 // to the lane's own block (its 32 code bytes in order).  tl: 128 chunks.
 __device__ __forceinline__ void stage_codes_in(u32x4* tl, uint32_t lane, CodeBlock<8>& blk) {
-  tl[swz8(lane)] = u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]};
-  tl[swz8(64 + lane)] = u32x4{blk.w[4], blk.w[5], blk.w[6], blk.w[7]};
+  const uint32_t rs = lane + (lane >> 4), bs = 2 * lane + (lane >> 3);
+  tl[rs] = u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]};
+  tl[rs + 68] = u32x4{blk.w[4], blk.w[5], blk.w[6], blk.w[7]};
   wave_lds_sync();
-  const u32x4 a = tl[swz8(2 * lane)], b = tl[swz8(2 * lane + 1)];
+  const u32x4 a = tl[bs], b = tl[bs + 1];
   wave_lds_sync();
   blk.w[0] = a.x; blk.w[1] = a.y; blk.w[2] = a.z; blk.w[3] = a.w;
   blk.w[4] = b.x; blk.w[5] = b.y; blk.w[6] = b.z; blk.w[7] = b.w;
@@ -776,10 +815,11 @@ __device__ __forceinline__ void stage_codes_in(u32x4* tl, uint32_t lane, CodeBlo
 // and tile + 1024 + 16 * lane.
 template <int NT>
 __device__ __forceinline__ void stage_codes_out(u32x4* tl, uint32_t lane, const CodeBlock<8>& blk, TileRef tile) {
-  tl[swz8(2 * lane)] = u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]};
-  tl[swz8(2 * lane + 1)] = u32x4{blk.w[4], blk.w[5], blk.w[6], blk.w[7]};
+  const uint32_t rs = lane + (lane >> 4), bs = 2 * lane + (lane >> 3);
+  tl[bs] = u32x4{blk.w[0], blk.w[1], blk.w[2], blk.w[3]};
+  tl[bs + 1] = u32x4{blk.w[4], blk.w[5], blk.w[6], blk.w[7]};
   wave_lds_sync();
-  const u32x4 a = tl[swz8(lane)], b = tl[swz8(64 + lane)];
+  const u32x4 a = tl[rs], b = tl[rs + 68];
   wave_lds_sync();
   st16<NT>(tile, 16 * lane, a);
   st16<NT>(tile, 1024 + 16 * lane, b);

@@ -149,8 +149,8 @@ constexpr int lds_chunks(int needed, int groups) {
              ? kLdsBytesPerCU / groups / (16 * kWavesPerGroup)
              : needed;
 }
-constexpr int kEncLdsChunks = lds_chunks(kChunks, QR_ENC_GROUPS_PER_CU);
-constexpr int kDecLdsChunks = lds_chunks(kChunks, QR_DEC_GROUPS_PER_CU_MAX);
+constexpr int kEncLdsChunks = lds_chunks(kTileSlots, QR_ENC_GROUPS_PER_CU);
+constexpr int kDecLdsChunks = lds_chunks(kTileSlots, QR_DEC_GROUPS_PER_CU_MAX);
 
 // ---------------------------------------------------------------------------
 // encode
@@ -176,13 +176,13 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restr
   load_tile(tile);
   for (; tile < ntiles; tile += stride) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) tl[swz(lane + kWave * k)] = v[k];
+    for (int k = 0; k < 4; ++k) tl[row_slot(lane, k)] = v[k];
     if (tile + stride < ntiles) load_tile(tile + stride);
     wave_lds_sync();
     uint32_t w[kBlockValues / 2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const u32x4 c = tl[swz(4 * lane + j)];
+      const u32x4 c = tl[block_slot(lane, j)];
       w[4 * j] = c.x; w[4 * j + 1] = c.y; w[4 * j + 2] = c.z; w[4 * j + 3] = c.w;
     }
     wave_lds_sync();  // the next tile overwrites this LDS tile
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restr
 // the wave's LDS tile.
 __device__ __forceinline__ void write_lane_words(u32x4* tl, uint32_t lane, const uint32_t (&w)[kBlockValues / 2]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) tl[swz(4 * lane + j)] = u32x4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+  for (int j = 0; j < 4; ++j) tl[block_slot(lane, j)] = u32x4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
 }
 
 // The same from 32 fp32 values, each rounded to the dtype (nearest even).
@@ -229,7 +229,7 @@ template <int NT>
 __device__ __forceinline__ void flush_tile(u32x4* tl, uint32_t lane, TileRef dst) {
   wave_lds_sync();
 #pragma unroll
-  for (int k = 0; k < 4; ++k) st16<NT>(dst, 16 * (lane + kWave * k), tl[swz(lane + kWave * k)]);
+  for (int k = 0; k < 4; ++k) st16<NT>(dst, 16 * (lane + kWave * k), tl[row_slot(lane, k)]);
   wave_lds_sync();
 }
 
@@ -284,7 +284,7 @@ struct ReduceArgs {
 // 2 KB staging region of 8-bit codes, which reuses the output tile's space.
 template <int BI, int BO, bool WITH_Y>
 constexpr int kReduceLdsChunks =
-    lds_chunks(WITH_Y ? kChunks : ((kStaged<BI> || kStaged<BO>) ? kChunks / 2 : 1), QR_RED_GROUPS_PER_CU_MAX);
+    lds_chunks(WITH_Y ? kTileSlots : ((kStaged<BI> || kStaged<BO>) ? kStageSlots : 1), QR_RED_GROUPS_PER_CU_MAX);
 
 // Every rank's block `lane` of tile `tile` (codes and scale) into registers.
 template <int BI, int R>
