@@ -496,11 +496,15 @@ def main():
     }
     if copy_ref:
         result["copy_ref"] = copy_ref
+    ok = True
     if not args.no_cpu_baseline:
         cb, ok = cpu_baseline(w, xs, out, y, args.cpu_seconds, args.cpu_threads or cpu_threads())
         result["cpu_baseline"] = cb
         result["parity_sample"] = ok
     print(json.dumps(result), flush=True)
+    if not ok:
+        print("bench.py: the GPU output differs from the oracle on the sampled tiles", file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -73,8 +73,7 @@ size_t qr_packed_bytes(qr_format fmt, size_t n) {
 
 qr_status qr_encode(qr_format fmt, qr_dtype dtype, const void* x, void* packed, size_t n, void* stream) {
   if (!tile_bytes(fmt) || (dtype != QR_FP16 && dtype != QR_BF16)) return QR_ERR_UNSUPPORTED;
-  if (n % kTileValues || too_large(n)) return QR_ERR_SIZE;
-  if (n == 0) return QR_OK;
+  if (n == 0 || n % kTileValues || too_large(n)) return QR_ERR_SIZE;
   if (!x || !packed) return QR_ERR_ARG;
   if (!aligned16(x) || !aligned16(packed)) return QR_ERR_ALIGN;
   const size_t pb = qr_packed_bytes(fmt, n);
@@ -93,8 +92,7 @@ qr_status qr_encode(qr_format fmt, qr_dtype dtype, const void* x, void* packed, 
 
 qr_status qr_decode(qr_format fmt, qr_dtype dtype, const void* packed, void* y, size_t n, void* stream) {
   if (!tile_bytes(fmt) || (dtype != QR_FP16 && dtype != QR_BF16)) return QR_ERR_UNSUPPORTED;
-  if (n % kTileValues || too_large(n)) return QR_ERR_SIZE;
-  if (n == 0) return QR_OK;
+  if (n == 0 || n % kTileValues || too_large(n)) return QR_ERR_SIZE;
   if (!packed || !y) return QR_ERR_ARG;
   if (!aligned16(packed) || !aligned16(y)) return QR_ERR_ALIGN;
   const size_t pb = qr_packed_bytes(fmt, n);
@@ -118,8 +116,7 @@ qr_status qr_reduce_compressed_mixed(qr_format fmt_in, qr_format fmt_out, qr_dty
       is_asym(fmt_in) != is_asym(fmt_out) || (fmt_in == QR_FP4) != (fmt_out == QR_FP4))
     return QR_ERR_UNSUPPORTED;
   if (R < 1 || R > QR_MAX_RANKS) return QR_ERR_ARG;
-  if (n % kTileValues || too_large(n)) return QR_ERR_SIZE;
-  if (n == 0) return QR_OK;
+  if (n == 0 || n % kTileValues || too_large(n)) return QR_ERR_SIZE;
   if (!packed_ranks || !packed_out) return QR_ERR_ARG;
   for (int r = 0; r < R; ++r)
     if (!packed_ranks[r]) return QR_ERR_ARG;

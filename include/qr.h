@@ -59,9 +59,9 @@
  *   decode: y = value(code) * d, exact in fp32, rounded to the I/O dtype.
  *
  * Conventions for every call:
- *   - `n` counts values and must be a multiple of 2048, of at most
- *     QR_MAX_TILES = 2^30 tiles (QR_ERR_SIZE otherwise); n == 0 is a valid empty call that
- *     launches nothing and returns QR_OK.
+ *   - `n` counts values and must be a positive multiple of 2048, of at most
+ *     QR_MAX_TILES = 2^30 tiles; any other n, 0 included, returns QR_ERR_SIZE
+ *     (the tile is the unit of the format, and an empty call is a caller error).
  *   - Buffer pointers are DEVICE pointers (hipMalloc or the PyTorch caching
  *     allocator), 16-byte aligned (QR_ERR_ALIGN), owned by the caller.  The
  *     library allocates nothing and keeps no state between calls.

@@ -1,5 +1,5 @@
 /* validate_check.c -- every argument check of include/qr.h from plain C, with
- * no GPU work: each call is rejected on the host, is an empty n == 0 call, or
+ * no GPU work: each call is rejected on the host (n == 0 included), or
  * passes the checks and reaches a launch function that this build replaces
  * with a stand-in (launch_stubs.cpp), so the pointers below are addresses
  * that are never dereferenced.  Built against a host-sanitized (AddressSanitizer and
@@ -68,7 +68,8 @@ static void encode_decode(void) {
     EXPECT(qr_encode(fmt, QR_FP16, CP(A), P(B + 4), n, NULL), QR_ERR_ALIGN);
     EXPECT(qr_encode(fmt, QR_FP16, CP(A), P(A + 2 * n - 16), n, NULL), QR_ERR_ALIAS);
     EXPECT(qr_encode(fmt, QR_FP16, CP(A + pb - 16), P(A), n, NULL), QR_ERR_ALIAS);
-    EXPECT(qr_encode(fmt, QR_FP16, NULL, NULL, 0, NULL), QR_OK);
+    EXPECT(qr_encode(fmt, QR_FP16, NULL, NULL, 0, NULL), QR_ERR_SIZE);
+    EXPECT(qr_encode(fmt, QR_FP16, CP(A), P(B), 0, NULL), QR_ERR_SIZE);
     EXPECT(qr_decode(fmt, (qr_dtype)-1, CP(A), P(B), n, NULL), QR_ERR_UNSUPPORTED);
     EXPECT(qr_decode(fmt, QR_FP16, CP(A), P(B), 100, NULL), QR_ERR_SIZE);
     EXPECT(qr_decode(fmt, QR_BF16, CP(A), P(B), huge, NULL), QR_ERR_SIZE);
@@ -77,7 +78,8 @@ static void encode_decode(void) {
     EXPECT(qr_decode(fmt, QR_FP16, CP(A + 2), P(B), n, NULL), QR_ERR_ALIGN);
     EXPECT(qr_decode(fmt, QR_FP16, CP(A), P(B + 8), n, NULL), QR_ERR_ALIGN);
     EXPECT(qr_decode(fmt, QR_FP16, CP(A), P(A + pb - 16), n, NULL), QR_ERR_ALIAS);
-    EXPECT(qr_decode(fmt, QR_FP16, NULL, NULL, 0, NULL), QR_OK);
+    EXPECT(qr_decode(fmt, QR_FP16, NULL, NULL, 0, NULL), QR_ERR_SIZE);
+    EXPECT(qr_decode(fmt, QR_FP16, CP(A), P(B), 0, NULL), QR_ERR_SIZE);
   }
   EXPECT(qr_encode((qr_format)7, QR_FP16, CP(A), P(B), 2048, NULL), QR_ERR_UNSUPPORTED);
   EXPECT(qr_decode((qr_format)0, QR_FP16, CP(A), P(B), 2048, NULL), QR_ERR_UNSUPPORTED);
@@ -105,8 +107,9 @@ static void reduce(void) {
   EXPECT(qr_reduce_compressed(QR_INT4, QR_FP16, ranks, 2, P(A + 512), P(C), n, NULL), QR_ERR_ALIAS);
   EXPECT(qr_reduce_compressed(QR_INT4, QR_FP16, ranks, 2, P(B), P(A + 0x100000 - 1024), n, NULL), QR_ERR_ALIAS);
   EXPECT(qr_reduce_compressed(QR_INT4, QR_FP16, ranks, 2, P(B), P(B + 1024), n, NULL), QR_ERR_ALIAS);
-  /* a rank buffer repeated is allowed; an empty call returns at once */
-  EXPECT(qr_reduce_compressed(QR_INT4, QR_FP16, ranks, 16, NULL, NULL, 0, NULL), QR_OK);
+  /* n == 0 is a size error, checked before the pointers */
+  EXPECT(qr_reduce_compressed(QR_INT4, QR_FP16, ranks, 16, NULL, NULL, 0, NULL), QR_ERR_SIZE);
+  EXPECT(qr_reduce_compressed(QR_INT4, QR_FP16, ranks, 2, P(B), P(C), 0, NULL), QR_ERR_SIZE);
   /* formats: unknown, or mixed across the families */
   EXPECT(qr_reduce_compressed((qr_format)5, QR_FP16, ranks, 2, P(B), P(C), n, NULL), QR_ERR_UNSUPPORTED);
   EXPECT(qr_reduce_compressed(QR_INT4, (qr_dtype)3, ranks, 2, P(B), P(C), n, NULL), QR_ERR_UNSUPPORTED);
@@ -116,7 +119,7 @@ static void reduce(void) {
   EXPECT(qr_reduce_compressed_mixed(QR_INT4, QR_FP4, QR_FP16, ranks, 2, P(B), P(C), n, NULL), QR_ERR_UNSUPPORTED);
   /* the mixed call sizes its output by the output format (2176 B per INT8 tile) */
   EXPECT(qr_reduce_compressed_mixed(QR_INT3, QR_INT8, QR_FP16, ranks, 1, P(A - 1024), NULL, n, NULL), QR_ERR_ALIAS);
-  EXPECT(qr_reduce_compressed_mixed(QR_INT4, QR_INT8, QR_BF16, ranks, 1, P(D), NULL, 0, NULL), QR_OK);
+  EXPECT(qr_reduce_compressed_mixed(QR_INT4, QR_INT8, QR_BF16, ranks, 1, P(D), NULL, 0, NULL), QR_ERR_SIZE);
 }
 
 /* Calls that pass every check reach the launch, which in this build is a
@@ -132,6 +135,8 @@ static void accepted(void) {
   EXPECT(qr_decode(QR_ASYM8, QR_FP16, CP(A), P(A + 4 * 2096), n, NULL), QR_ERR_HIP);
   EXPECT(qr_decode(QR_FP4, QR_BF16, CP(A), P(B), n, NULL), QR_ERR_HIP);
   EXPECT(qr_reduce_compressed_mixed(QR_INT3, QR_INT8, QR_FP16, ranks, 1, P(A + 896), NULL, 2048, NULL), QR_ERR_HIP);
+  /* an INT3 output (896 B) that ends where the INT4 input starts */
+  EXPECT(qr_reduce_compressed_mixed(QR_INT4, QR_INT3, QR_FP16, ranks, 1, P(A - 896), NULL, 2048, NULL), QR_ERR_HIP);
   EXPECT(qr_reduce_compressed(QR_ASYM8, QR_FP16, ranks, QR_MAX_RANKS, P(B), P(C), n, NULL), QR_ERR_HIP);
   EXPECT(qr_reduce_compressed(QR_FP4, QR_BF16, same, 3, P(B), NULL, n, NULL), QR_ERR_HIP);
   EXPECT(qr_reduce_compressed_mixed(QR_ASYM8, QR_ASYM4, QR_BF16, ranks, 2, P(B), P(B + 4 * 1072), n, NULL),

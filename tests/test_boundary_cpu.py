@@ -86,8 +86,9 @@ def test_encode_validation(L):
     # packed starts inside x (x spans 2*n bytes), or x starts inside packed
     assert enc(L, x=A, p=A + 4096 - 16) == qr.QR_ERR_ALIAS
     assert enc(L, x=A + 1152 - 16, p=A) == qr.QR_ERR_ALIAS
-    # the empty call is valid and launches nothing, whatever the pointers
-    assert enc(L, n=0, x=0, p=0) == qr.QR_OK
+    # n == 0 is a size error, whatever the pointers (the size is checked first)
+    assert enc(L, n=0, x=0, p=0) == qr.QR_ERR_SIZE
+    assert enc(L, n=0) == qr.QR_ERR_SIZE
 
 
 def test_decode_validation(L):
@@ -98,7 +99,8 @@ def test_decode_validation(L):
     assert dec(L, y=0) == qr.QR_ERR_ARG
     assert dec(L, y=B + 4) == qr.QR_ERR_ALIGN
     assert dec(L, p=A, y=A + 1024) == qr.QR_ERR_ALIAS
-    assert dec(L, n=0, p=0, y=0) == qr.QR_OK
+    assert dec(L, n=0, p=0, y=0) == qr.QR_ERR_SIZE
+    assert dec(L, n=0) == qr.QR_ERR_SIZE
 
 
 def test_reduce_validation(L):
@@ -117,7 +119,7 @@ def test_reduce_validation(L):
     assert red(L, ranks=[A, B - 512]) == qr.QR_ERR_ALIAS     # a rank overlaps packed_out
     assert red(L, y=A + 1024) == qr.QR_ERR_ALIAS             # y_out overlaps a rank
     assert red(L, out=C + 2048) == qr.QR_ERR_ALIAS           # outputs overlap each other
-    assert red(L, n=0, ranks=[0], out=0, y=0) == qr.QR_OK
+    assert red(L, n=0, ranks=[0], out=0, y=0) == qr.QR_ERR_SIZE
 
 
 def test_binding_rejects_host_tensors():
@@ -145,8 +147,7 @@ def test_reduce_mixed_validation(L):
     assert redm(L, fi=4, fo=8, out=A - 2048) == qr.QR_ERR_ALIAS
     assert redm(L, fi=4, fo=8, out=A + 1152 - 16) == qr.QR_ERR_ALIAS
     assert redm(L, fi=8, fo=3, out=A + 2176 - 16) == qr.QR_ERR_ALIAS
-    assert redm(L, fi=4, fo=3, ranks=[A], out=A - 896, y=0, n=0) == qr.QR_OK
-    assert redm(L, n=0, ranks=[0], out=0, y=0) == qr.QR_OK
+    assert redm(L, n=0, ranks=[0], out=0, y=0) == qr.QR_ERR_SIZE
 
 
 def test_asym_validation(L):
@@ -162,7 +163,7 @@ def test_asym_validation(L):
     assert redm(L, fi=20, fo=24, out=A - 2048) == qr.QR_ERR_ALIAS
     assert redm(L, fi=20, fo=24, out=A + 1072 - 16) == qr.QR_ERR_ALIAS
     assert redm(L, fi=24, fo=20, out=A + 2096 - 16) == qr.QR_ERR_ALIAS
-    assert redm(L, fi=20, fo=20, n=0, ranks=[0], out=0, y=0) == qr.QR_OK
+    assert redm(L, fi=20, fo=20, n=0, ranks=[0], out=0, y=0) == qr.QR_ERR_SIZE
 
 
 def test_fp4_validation(L):
@@ -173,7 +174,7 @@ def test_fp4_validation(L):
     for fi, fo in ((4, 36), (36, 4), (36, 20), (24, 36), (36, 8)):
         assert redm(L, fi=fi, fo=fo) == qr.QR_ERR_UNSUPPORTED, (fi, fo)
     assert redm(L, fi=36, fo=36, out=A - 1152 + 16) == qr.QR_ERR_ALIAS
-    assert redm(L, fi=36, fo=36, n=0, ranks=[0], out=0, y=0) == qr.QR_OK
+    assert redm(L, fi=36, fo=36, n=0, ranks=[0], out=0, y=0) == qr.QR_ERR_SIZE
 
 
 def test_too_many_tiles(L):

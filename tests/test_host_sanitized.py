@@ -4,7 +4,7 @@ UndefinedBehaviorSanitizer (host code only; CPU only).
 qr_api.hip is compiled with the sanitizers on its host side and linked with
 stand-ins for the launch functions of the other translation units
 (tests/c_abi/launch_stubs.cpp); tests/c_abi/validate_check.c then drives every
-rejection path of include/qr.h, the empty calls and a set of accepted calls,
+rejection path of include/qr.h (n == 0 among them) and a set of accepted calls,
 which end in a stand-in instead of a launch.  No GPU work runs."""
 import os
 import subprocess

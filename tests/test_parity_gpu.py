@@ -7,8 +7,10 @@ dtype for those; every step is a correctly rounded IEEE operation, so exact
 equality is what is expected and what is asserted).  Sizes span several
 tiles, waves and workgroups, with a ragged last workgroup; the full-size
 workloads are checked on sampled tiles, which the oracle computes one by one
-(tiles are independent), plus properties that hold at any size.
+(tiles are independent), plus properties that hold at any size, and the bench
+workload and the INT3 two-rank reduce on every tile of seed 0.
 """
+import os
 import sys
 
 import numpy as np
@@ -281,6 +283,67 @@ def test_workload_full_size_sampled(qa, oracle, name, seed):
     check_tiles(oracle, w, xs_t, packed_full, out_host, y_host, tiles)
 
 
+# Workloads whose whole full-size output is checked against the oracle, tile
+# by tile: the bench workload and the INT3 two-rank reduce.
+EVERY_TILE_CASES = ["int4_r8_fp16_32x1024x4096", "int3_r2_fp16_32x1024x4096"]
+
+
+def _host_threads():
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return max(1, min(16, os.cpu_count() or 1))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", EVERY_TILE_CASES)
+def test_workload_full_size_every_tile(qa, oracle, name):
+    """Every byte of the full-size outputs (each rank's packed buffer, the
+    re-encoded sum and the decoded sum) of seed 0 against the oracle.  The
+    oracle runs on the host over contiguous tile ranges in parallel threads
+    (its C calls release the GIL)."""
+    import threading
+
+    w = W.WORKLOADS[name]
+    log(f"every tile: workload {name} n={w.n} R={w.ranks} seed=0")
+    xs = W.inputs(w, seed=0, device="cuda")
+    packed, out, y = run_pipeline(qa, w, xs)
+    torch.cuda.synchronize()
+    xs_h = [u16(x) for x in xs]
+    packed_h = [p.cpu().numpy() for p in packed]
+    out_h, y_h = out.cpu().numpy(), u16(y)
+    del xs, packed, out, y
+    torch.cuda.empty_cache()
+    bits, bits_out = BITS[w.fmt], BITS[w.out_fmt]
+    tb, tbo = oracle.packed_bytes(bits, 2048), oracle.packed_bytes(bits_out, 2048)
+    ntiles = w.n // 2048
+    threads = _host_threads()
+    bounds = [ntiles * k // threads for k in range(threads + 1)]
+    bad = [None] * threads
+
+    def work(k):
+        a, b = bounds[k], bounds[k + 1]
+        sv = slice(a * 2048, b * 2048)
+        wr = [oracle.encode(bits, w.io_dtype, xh[sv]) for xh in xs_h]
+        for r in range(w.ranks):
+            if not np.array_equal(packed_h[r][a * tb:b * tb], wr[r]):
+                bad[k] = f"rank {r} encode differs in tiles [{a}, {b})"
+                return
+        wout, wy = oracle.reduce_mixed(bits, bits_out, w.io_dtype, wr, (b - a) * 2048)
+        if not np.array_equal(out_h[a * tbo:b * tbo], wout):
+            bad[k] = f"re-encoded sum differs in tiles [{a}, {b})"
+        elif not np.array_equal(y_h[sv], wy):
+            bad[k] = f"decoded sum differs in tiles [{a}, {b})"
+
+    pool = [threading.Thread(target=work, args=(k,)) for k in range(threads)]
+    for t in pool:
+        t.start()
+    for t in pool:
+        t.join()
+    log(f"every tile: {ntiles} tiles checked on {threads} host threads")
+    assert all(b is None for b in bad), [b for b in bad if b]
+
+
 def test_block_scale_every_fp16_scale():
     """The library's block-scale device function over every positive finite
     fp16 scale d (block maximum Q*d): scale bits d and encode multiplier equal
@@ -339,15 +402,21 @@ def test_reduce_mixed_parity(qa, oracle, fi, fo, dtype, R):
     assert np.array_equal(out2.cpu().numpy(), wout)
 
 
-def test_empty_calls(qa):
-    """n = 0 through every entry point: nothing is launched, no error."""
+def test_empty_calls_are_size_errors(qa):
+    """n = 0 through every entry point: rejected with QR_ERR_SIZE on the host
+    (the tile is the unit), nothing is launched."""
     e16 = torch.empty(0, dtype=torch.float16, device="cuda")
     e8 = torch.empty(0, dtype=torch.uint8, device="cuda")
-    assert qa.qr_encode("int4", e16, e8).numel() == 0
-    assert qa.qr_decode("int3", e8, 0, torch.float16, y=e16).numel() == 0
-    out, y = qa.qr_reduce_compressed("int8", torch.bfloat16, [e8, e8], 0, packed_out=e8,
-                                     y_out=torch.empty(0, dtype=torch.bfloat16, device="cuda"))
-    out, y = qa.qr_reduce_compressed_mixed("int4", "int8", torch.float16, [e8], 0, packed_out=e8, y_out=e16)
+    calls = [lambda: qa.qr_encode("int4", e16, e8),
+             lambda: qa.qr_decode("int3", e8, 0, torch.float16, y=e16),
+             lambda: qa.qr_reduce_compressed("int8", torch.bfloat16, [e8, e8], 0, packed_out=e8,
+                                             y_out=torch.empty(0, dtype=torch.bfloat16, device="cuda")),
+             lambda: qa.qr_reduce_compressed_mixed("int4", "int8", torch.float16, [e8], 0, packed_out=e8,
+                                                   y_out=e16)]
+    for call in calls:
+        with pytest.raises(qa.QRError) as ei:
+            call()
+        assert ei.value.status == qa.QR_ERR_SIZE
     torch.cuda.synchronize()
 
 
