@@ -622,21 +622,29 @@ __device__ __forceinline__ uint32_t group_params(float lo, float hi, float& d, f
   return (uint32_t)__builtin_bit_cast(uint16_t, dh) | ((uint32_t)z << 16);
 }
 
-// Code of one value, q = clamp(rint(v) + z, 0, qmax), as the bits of 2^23 + q
-// (low byte = q); zb = z - 256.  Adding 2^23 + 256 (even) rounds v to an
-// integer with ties to even for every v >= -256; adding z first would move
-// ties for odd z.  Smaller v, and large v, land outside [2^23, 2^23 + qmax]
-// and clamp to the ends, as the clamp of rint(v) + z does.
+// Code of one value, q = clamp(rint(v) + z, 0, qmax), as the bits of
+// B + q with B = 2^23 + 0x6400 (low byte = q, 0x64 above it, as quantize());
+// zb = z - 256.  Adding B + 256 (even) rounds v to an integer with ties to
+// even for every v >= -(0x6400 + 256); adding z first would move ties for
+// odd z.  Smaller v, and large v, land outside [B, B + qmax] and clamp to the
+// ends, as the clamp of rint(v) + z does.
 template <int F>
 __device__ __forceinline__ uint32_t quantize_asym(float v, float zb) {
-  const float r = v + 8388864.0f;  // 2^23 + 256
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(r + zb, 8388608.0f,
-                                                              8388608.0f + Format<F>::kQmax));
+  const float r = v + (kMagicBase + 256.0f);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(r + zb, kMagicBase, kMagicBase + Format<F>::kQmax));
 }
 
-// (q - z) as fp32 from quantize_asym()'s result; zm = 2^23 + z (exact).
+// (q - z) as fp32 from quantize_asym()'s result; zm = B + z (exact).
 __device__ __forceinline__ float code_value_asym(uint32_t t, float zm) {
   return __builtin_bit_cast(float, t) - zm;
+}
+
+// fp16 pair dtype_RNE((q0 - z) * s), dtype_RNE((q1 - z) * s) from two
+// quantize_asym() results, the zero point z and the fp16 scale s (as
+// decode_pair_fp16: the exact code difference times s, rounded once).
+__device__ __forceinline__ uint32_t decode_pair_asym_fp16(uint32_t t0, uint32_t t1, f16x2 nzb, f16x2 s2) {
+  const f16x2 k = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(t1, t0, 0x05040100u)) + nzb;
+  return __builtin_bit_cast(uint32_t, k * s2);
 }
 
 // Quantizes one lane's block of a group given as 16 packed fp16/bf16 words;

@@ -131,9 +131,10 @@ namespace qr {
 #ifndef QR_RED_GROUPS_PER_CU_MAX
 #define QR_RED_GROUPS_PER_CU_MAX 5
 #endif
-// Decode workgroups resident on one CU at a time (0: no limit).
+// Decode workgroups resident on one CU at a time (0: no limit); per
+// 134M-value INT4 fp16 rank 56.4 -> 53.8 us at 5 workgroups (20 waves).
 #ifndef QR_DEC_GROUPS_PER_CU_MAX
-#define QR_DEC_GROUPS_PER_CU_MAX 0
+#define QR_DEC_GROUPS_PER_CU_MAX 5
 #endif
 constexpr int kWavesPerGroup = QR_WAVES_PER_GROUP;
 constexpr int kThreads = kWave * kWavesPerGroup;
@@ -152,6 +153,33 @@ constexpr int lds_chunks(int needed, int groups) {
 constexpr int kEncLdsChunks = lds_chunks(kTileSlots, QR_ENC_GROUPS_PER_CU);
 constexpr int kDecLdsChunks = lds_chunks(kTileSlots, QR_DEC_GROUPS_PER_CU_MAX);
 
+// 1: workgroups of formats whose tiles are not whole 128-byte cache lines
+// take their tiles in XCD pairs (group_index()); 0: in dispatch order.
+#ifndef QR_XCD_PAIRS
+#define QR_XCD_PAIRS 1
+#endif
+
+// Index, in tile order, of workgroup b of a grid of `grid`.  Workgroups are
+// dealt to the 8 XCDs in turn (workgroup b runs on XCD b % 8), each with its
+// own L2.  When a tile is not a whole number of 128-byte lines (TB1 or TB2
+// bytes), adjacent tiles share a line, and only the boundaries of aligned
+// groups of 8 tiles fall on line boundaries.  The two workgroups (of 4 tiles
+// each) that cover such a group are then workgroups b and b + 8 of a window of
+// 16, which run on one XCD, so that no line is split between two L2s.  The
+// last, partial window keeps the dispatch order.
+template <int TB1, int TB2>
+__device__ __forceinline__ int group_index(int b, int grid) {
+  if constexpr (!QR_XCD_PAIRS || kWavesPerGroup != 4 || (TB1 % 128 == 0 && TB2 % 128 == 0)) {
+    return b;
+  } else {
+    static_assert((8 * TB1) % 128 == 0 && (8 * TB2) % 128 == 0, "8 tiles span whole lines");
+    const int win = b & ~15;
+    if (win + 16 > grid) return b;
+    const int r = b & 15;
+    return win + 2 * (r & 7) + (r >> 3);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // encode
 // ---------------------------------------------------------------------------
@@ -164,7 +192,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restr
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
   u32x4* tl = lds[wave];
   const int stride = gridDim.x * kWavesPerGroup;
-  int tile = blockIdx.x * kWavesPerGroup + wave;
+  constexpr int TB = Format<BITS>::kTileBytes;
+  int tile = group_index<TB, TB>(blockIdx.x, gridDim.x) * kWavesPerGroup + wave;
   if (tile >= ntiles) return;
   // the next tile's 4 KB is loaded into registers while this one is encoded
   u32x4 v[4];
@@ -239,7 +268,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint8_t* __restr
   __shared__ u32x4 lds[kWavesPerGroup][kDecLdsChunks];
   const uint32_t lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
-  for (int tile = blockIdx.x * kWavesPerGroup + wave; tile < ntiles; tile += gridDim.x * kWavesPerGroup) {
+  constexpr int TB = Format<BITS>::kTileBytes;
+  for (int tile = group_index<TB, TB>(blockIdx.x, gridDim.x) * kWavesPerGroup + wave; tile < ntiles;
+       tile += gridDim.x * kWavesPerGroup) {
     Block<BITS> blk;
     uint32_t scale;
     load_block<BITS, QR_DEC_LOAD_POL>(tile_ref(packed + (size_t)tile * Format<BITS>::kTileBytes, Format<BITS>::kTileBytes),
@@ -390,10 +421,18 @@ __device__ __forceinline__ void reduce_tile(const ReduceArgs& a, int tile, uint3
       t[i + 1] = quantize_asym<BO>(v1, zb);
     }
     if constexpr (WITH_Y) {  // decode of the re-encoded sum, straight from the codes
-      const float zm = 8388608.0f + z;
+      if constexpr (DT == kFp16 && QR_Y_HALF_PAIRS) {
+        const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)scale);
+        const _Float16 nz = -(_Float16)(1024.0f + z);  // exact: 1024 + z < 2048
 #pragma unroll
-      for (int i = 0; i < kBlockValues; i += 2)
-        yw[i / 2] = pack2<DT>(code_value_asym(t[i], zm) * d, code_value_asym(t[i + 1], zm) * d);
+        for (int i = 0; i < kBlockValues; i += 2)
+          yw[i / 2] = decode_pair_asym_fp16(t[i], t[i + 1], f16x2{nz, nz}, f16x2{sh, sh});
+      } else {
+        const float zm = kMagicBase + z;
+#pragma unroll
+        for (int i = 0; i < kBlockValues; i += 2)
+          yw[i / 2] = pack2<DT>(code_value_asym(t[i], zm) * d, code_value_asym(t[i + 1], zm) * d);
+      }
     }
     pack_block<BO>(t, ob);
   } else if constexpr (Format<BO>::kFp4) {
@@ -468,7 +507,8 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
   const uint32_t lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
   const int stride = gridDim.x * kWavesPerGroup;
-  int tile = blockIdx.x * kWavesPerGroup + wave;
+  int tile = group_index<Format<BI>::kTileBytes, Format<BO>::kTileBytes>(blockIdx.x, gridDim.x) * kWavesPerGroup +
+             wave;
   if constexpr (QR_RED_PREFETCH) {
     // Each wave loops over several tiles with two register sets: the next
     // tile's loads are in flight while the current tile is reduced.
