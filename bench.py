@@ -289,6 +289,9 @@ def main():
                          "calibration kernel for the HBM traffic counters)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--lib", default=None,
+                    help="load this build of libqr.so instead of the package's (a compile-time variant "
+                         "made with python -m bit_quantized_all_amd.build --out PATH -DNAME=VALUE)")
     args = ap.parse_args()
 
     if args.ingest_pmc:
@@ -306,6 +309,9 @@ def main():
     import bit_quantized_all_amd as qa
     import workloads as W
 
+    if args.lib:
+        from bit_quantized_all_amd import qr as _qr
+        _qr.LIB_PATH = os.path.abspath(args.lib)
     name = args.workload or W.BENCH_WORKLOAD
     w = W.WORKLOADS[name]
     if args.values is not None:
@@ -458,16 +464,18 @@ def main():
     fp16_input = w.ranks * w.n * 2
     value = fp16_input / (ms_per_step * 1e-3) / 1e9
     pipe_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # stored counter traffic belongs to the default build of the current sources
+    traffic = (lambda k: None) if args.lib else (lambda k: traffic_from_profiles(k, name))
     kernels = {}
     for k, us in kern_us.items():
         g = ab[k] / (us * 1e-6) / 1e9
         kernels[k] = {"us_per_launch": round(us, 3), "launches_per_step": launches[k],
                       "algorithmic_bytes": int(ab[k]), "achieved_gbs": round(g, 1),
-                      "frac": round(g / PEAK_HBM_GBS, 4), "traffic": traffic_from_profiles(k, name)}
+                      "frac": round(g / PEAK_HBM_GBS, 4), "traffic": traffic(k)}
     dom = max(kern_us, key=lambda k: kern_us[k] * launches[k])
     roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["achieved_gbs"],
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": kernels[dom]["frac"],
-                "traffic": traffic_from_profiles(dom, name)}
+                "traffic": traffic(dom)}
 
     result = {
         "metric": METRIC,
@@ -496,6 +504,8 @@ def main():
     }
     if copy_ref:
         result["copy_ref"] = copy_ref
+    if args.lib:
+        result["library"] = os.path.abspath(args.lib)
     ok = True
     if not args.no_cpu_baseline:
         cb, ok = cpu_baseline(w, xs, out, y, args.cpu_seconds, args.cpu_threads or cpu_threads())

@@ -94,5 +94,21 @@ def build_test_helpers(quiet=True):
     return build(out=TEST_HELPER_LIB, sources=TEST_HELPER_SRCS, quiet=quiet)
 
 
+def main(argv=None):
+    """python -m bit_quantized_all_amd.build [--out PATH] [-DNAME=VALUE ...]:
+    build the library (by default in place); definitions select the
+    compile-time variants of the kernels (the macros of csrc/qr_kernels.hpp
+    and csrc/qr_codec.hpp), e.g. for a measurement of a variant next to the
+    default build (bench.py --lib PATH)."""
+    import argparse
+    ap = argparse.ArgumentParser(description=main.__doc__)
+    ap.add_argument("--out", default=LIB)
+    args, defs = ap.parse_known_args(argv)
+    bad = [d for d in defs if not d.startswith("-D")]
+    if bad:
+        ap.error(f"unexpected arguments {bad} (only -DNAME=VALUE definitions)")
+    print(build(out=os.path.abspath(args.out), extra=defs, quiet=False))
+
+
 if __name__ == "__main__":
-    print(build(quiet=False))
+    main()

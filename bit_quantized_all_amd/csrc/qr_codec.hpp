@@ -56,6 +56,14 @@ enum { kFp16 = 0, kBf16 = 1 };
 // (FP4 E2M1 codes in 32-value blocks).
 template <int F>
 struct Format;
+// 1: the reduce loads each INT3 rank tile with one 16-byte load per lane and
+// hands the blocks out through LDS (stage_int3_in()); 0: each lane loads its
+// own block's planes and scale (8 + 4 + 2 bytes).  Measured slower; kept for
+// comparison.
+#ifndef QR_INT3_LDS_STAGE
+#define QR_INT3_LDS_STAGE 0
+#endif
+
 // 1: INT3 codes decode through a byte table (one permute maps four 3-bit
 // codes to the FP8 E4M3 values of code - 4, one conversion turns two of them
 // into fp32); 0: through signed bytes 32 * (code - 4).
@@ -861,6 +869,22 @@ __device__ __forceinline__ void load_block(TileRef tile, uint32_t g, Block<F>& b
   } else {
     scale = ld2<NT>(tile, Format<F>::kScaleOffset + 2 * g);
   }
+}
+
+// An INT3 tile held as 16 bytes per lane (bytes 16g .. 16g + 15 in lane g;
+// lanes 56..63, past the tile, hold zeros) to lane g's block and scale,
+// through the wave's LDS.
+__device__ __forceinline__ void stage_int3_in(u32x4* tl, uint32_t g, u32x4 raw, CodeBlock<3>& blk, uint32_t& scale) {
+  tl[g] = raw;
+  wave_lds_sync();
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(tl);
+  const uint32_t l0 = w[2 * g], l1 = w[2 * g + 1], h = w[Format<3>::kHighOffset / 4 + g];
+  const uint32_t s = reinterpret_cast<const uint16_t*>(tl)[Format<3>::kScaleOffset / 2 + g];
+  wave_lds_sync();
+  blk.low[0] = l0;
+  blk.low[1] = l1;
+  blk.high = h;
+  scale = s;
 }
 
 // Scale bits | zero point << 16 of the group of lane g's block, from the

@@ -233,6 +233,79 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restr
   }
 }
 
+// 1: INT3 and INT4 encode with an 8-lane group per 32-value block (4 values
+// per lane): the block maximum is a three-step DPP reduction over the group,
+// every lane derives the scale, and the packed tile is assembled in LDS from
+// each lane's bits, then stored coalesced.  0: one lane per block (the
+// default).  Measured slower; kept for comparison.
+#ifndef QR_ENC_GROUP8
+#define QR_ENC_GROUP8 0
+#endif
+
+// Maximum of v over the 8 lanes of an aligned group (DPP quad permutes
+// [1,0,3,2], [2,3,0,1], then the half-row mirror lane i <-> 7 - i).
+__device__ __forceinline__ int group8_max_i32(int v) {
+  v = __builtin_elementwise_max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+  v = __builtin_elementwise_max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
+  return __builtin_elementwise_max(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false));
+}
+
+template <int BITS, int DT>
+__global__ __launch_bounds__(kThreads) void encode_group8_kernel(const uint8_t* __restrict__ x,
+                                                                 uint8_t* __restrict__ packed, int ntiles) {
+  static_assert(BITS == 3 || BITS == 4, "symmetric 3- and 4-bit codes");
+  constexpr int TB = Format<BITS>::kTileBytes;
+  __shared__ u32x4 lds[kWavesPerGroup][kEncLdsChunks];
+  const uint32_t lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
+  u32x4* tl = lds[wave];
+  uint8_t* sb = reinterpret_cast<uint8_t*>(tl);
+  for (int tile = blockIdx.x * kWavesPerGroup + wave; tile < ntiles; tile += gridDim.x * kWavesPerGroup) {
+    const TileRef src = tile_ref(x + (size_t)tile * (kTileValues * 2), kTileValues * 2);
+    u32x2 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ld8<QR_ENC_LOAD_POL>(src, 512 * i + 8 * lane);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // values 256 i + 4 lane .. + 3: block 8 i + lane / 8, unit 32 i + lane / 2
+      const uint32_t w[2] = {v[i].x, v[i].y};
+      u16x2 m2 = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w[0] & 0x7fff7fffu),
+                                            __builtin_bit_cast(u16x2, w[1] & 0x7fff7fffu));
+      const int mb = group8_max_i32(m2.x > m2.y ? m2.x : m2.y);
+      float d, e;
+      const uint32_t sbits = block_scale<BITS>(half_pattern_to_f32<DT>((uint32_t)mb), d, e);
+      uint32_t t[4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float v0, v1;
+        scale_pair<DT>(w[j], e, v0, v1);
+        t[2 * j] = quantize<BITS>(v0);
+        t[2 * j + 1] = quantize<BITS>(v1);
+      }
+      const uint32_t c = lo_pair(t[0], t[1]) | hi_pair(t[2], t[3]);  // bytes q0 q1 q2 q3
+      const uint32_t unit = 32 * i + (lane >> 1);
+      if constexpr (BITS == 4) {
+        const uint32_t h = (c & 0xFu) | ((c >> 4) & 0xF0u) | ((c >> 8) & 0xF00u) | ((c >> 12) & 0xF000u);
+        *reinterpret_cast<uint16_t*>(sb + 4 * unit + 2 * (lane & 1)) = (uint16_t)h;
+      } else {
+        const uint32_t lo = (c & 3u) | ((c >> 6) & 0xCu) | ((c >> 12) & 0x30u) | ((c >> 18) & 0xC0u);
+        const uint32_t hi = ((c >> 2) & 1u) | ((c >> 9) & 2u) | ((c >> 16) & 4u) | ((c >> 23) & 8u);
+        sb[2 * unit + (lane & 1)] = (uint8_t)lo;
+        const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, 0xB1, 0xF, 0xF, false);
+        sb[Format<3>::kHighOffset + unit] = (uint8_t)((lane & 1) ? (other | (hi << 4)) : (hi | (other << 4)));
+      }
+      if ((lane & 7) == 0)
+        *reinterpret_cast<uint16_t*>(sb + Format<BITS>::kScaleOffset + 2 * (8 * i + (lane >> 3))) = (uint16_t)sbits;
+    }
+    wave_lds_sync();
+    const TileRef tp = tile_ref(packed + (size_t)tile * TB, TB);
+#pragma unroll
+    for (int k = 0; k < (TB + 16 * kWave - 1) / (16 * kWave); ++k)
+      st16<QR_ENC_STORE_POL>(tp, 16 * (lane + kWave * k), tl[lane + kWave * k]);  // past the tile: dropped
+    wave_lds_sync();
+  }
+}
+
 // ---------------------------------------------------------------------------
 // decode
 // ---------------------------------------------------------------------------
@@ -314,8 +387,10 @@ struct ReduceArgs {
 // LDS chunks per reduce wave: the fp16/bf16 output tile (WITH_Y) and / or the
 // 2 KB staging region of 8-bit codes, which reuses the output tile's space.
 template <int BI, int BO, bool WITH_Y>
-constexpr int kReduceLdsChunks =
-    lds_chunks(WITH_Y ? kTileSlots : ((kStaged<BI> || kStaged<BO>) ? kStageSlots : 1), QR_RED_GROUPS_PER_CU_MAX);
+constexpr int kReduceLdsChunks = lds_chunks(
+    WITH_Y ? kTileSlots
+           : ((kStaged<BI> || kStaged<BO>) ? kStageSlots : ((Format<BI>::kCodeBits == 3 && QR_INT3_LDS_STAGE) ? 64 : 1)),
+    QR_RED_GROUPS_PER_CU_MAX);
 
 // Every rank's block `lane` of tile `tile` (codes and scale) into registers.
 template <int BI, int R>
@@ -536,8 +611,20 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     for (; tile < a.ntiles; tile += stride) {
       Block<BI> blk[R];
       uint32_t sc[R];
-      load_ranks<BI, R>(a, tile, lane, blk, sc);
-      if constexpr (kLoadsFirst<BI, R>) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (Format<BI>::kCodeBits == 3 && QR_INT3_LDS_STAGE) {
+        // every rank's tile in one 16-byte load per lane, then handed out
+        // through LDS rank by rank before the decode starts
+        u32x4 raw[R];
+        const size_t toff = (size_t)tile * Format<BI>::kTileBytes;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          raw[r] = ld16<QR_RED_LOAD_POL>(tile_ref(a.ranks[r] + toff, Format<BI>::kTileBytes), 16 * lane);
+#pragma unroll
+        for (int r = 0; r < R; ++r) stage_int3_in(lds[wave], lane, raw[r], blk[r], sc[r]);
+      } else {
+        load_ranks<BI, R>(a, tile, lane, blk, sc);
+        if constexpr (kLoadsFirst<BI, R>) __builtin_amdgcn_sched_barrier(0);
+      }
       reduce_tile<BI, BO, DT, R, WITH_Y>(a, tile, lane, lds[wave], blk, sc);
     }
   }
@@ -576,6 +663,10 @@ Launch<P...> launch(void (*kernel)(P...)) {
 
 template <int BITS>
 qr_status launch_encode(int dt, const void* x, void* p, size_t ntiles, hipStream_t st) {
+  if constexpr (QR_ENC_GROUP8 && (BITS == 3 || BITS == 4)) {
+    auto k = dt == kFp16 ? launch(encode_group8_kernel<BITS, kFp16>) : launch(encode_group8_kernel<BITS, kBf16>);
+    return k(grid_for(ntiles), st, (const uint8_t*)x, (uint8_t*)p, (int)ntiles);
+  }
   const dim3 grid = grid_for((ntiles + QR_ENC_TILES_PER_WAVE - 1) / QR_ENC_TILES_PER_WAVE);
   auto k = dt == kFp16 ? launch(encode_kernel<BITS, kFp16>) : launch(encode_kernel<BITS, kBf16>);
   return k(grid, st, (const uint8_t*)x, (uint8_t*)p, (int)ntiles);

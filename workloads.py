@@ -36,6 +36,8 @@ tiles):
   int4_fp16_codec_32x1024x4096  encode + decode only of rank 0's input of the
                            [32 x 1024 x 4096] INT4 workload (the receive side's
                            decode of gathered tiles, at full size).
+  int3_fp16_codec_32x1024x4096  the same for INT3, on rank 0's input of the
+                           INT3 two-rank workload.
 
 Random numbers come from torch's seeded generators (Philox on the GPU, the CPU
 generator on the host); each (seed, workload, rank) gets its own stream seed.
@@ -126,6 +128,10 @@ WORKLOADS = {
                                              32 * 1024 * 4096, (32, 1024, 4096),
                                              channel_sigma=(0.01, 20.0), reduce=False,
                                              data_key="int4_r8_fp16_32x1024x4096"),
+    "int3_fp16_codec_32x1024x4096": Workload("int3_fp16_codec_32x1024x4096", "int3", torch.float16, 1,
+                                             32 * 1024 * 4096, (32, 1024, 4096),
+                                             channel_sigma=(0.01, 20.0), reduce=False,
+                                             data_key="int3_r2_fp16_32x1024x4096"),
 }
 
 BENCH_WORKLOAD = "int4_r8_fp16_32x1024x4096"
