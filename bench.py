@@ -52,8 +52,12 @@ def kernel_source_hash():
         h.update(p.encode())
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
-    h.update(repr(hip_build.FLAGS).encode())
-    h.update(repr([(os.path.basename(src), defs) for src, defs in hip_build.SOURCES]).encode())
+    # paths inside the repository enter relative to it, so a copy of the tree
+    # elsewhere has the same hash
+    def rel(a):
+        return os.path.relpath(a, hip_build.ROOT) if os.path.isabs(a) else a
+    h.update(repr([rel(f) for f in hip_build.FLAGS]).encode())
+    h.update(repr([(rel(src), defs) for src, defs in hip_build.SOURCES]).encode())
     return h.hexdigest()[:16]
 
 

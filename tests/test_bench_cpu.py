@@ -144,3 +144,20 @@ def test_kernel_source_hash_covers_every_source_and_the_build_flags(monkeypatch)
     assert bench.kernel_source_hash() == base
     monkeypatch.setattr(hip_build, "SOURCES", hip_build.SOURCES[:-1])
     assert bench.kernel_source_hash() != base
+
+
+def test_kernel_source_hash_is_the_same_for_a_copy_of_the_tree(monkeypatch):
+    """The build's flags name include directories by absolute path; the key
+    takes them relative to the repository, so a copy of the tree at another
+    path (where the benchmark runs) finds the counters stored here."""
+    from bit_quantized_all_amd import build as hip_build
+    base = bench.kernel_source_hash()
+    other = "/elsewhere/copy"
+
+    def moved(a):
+        return other + a[len(hip_build.ROOT):] if isinstance(a, str) and a.startswith(hip_build.ROOT) else a
+    monkeypatch.setattr(hip_build, "FLAGS", [moved(f) for f in hip_build.FLAGS])
+    monkeypatch.setattr(hip_build, "SOURCES", [(moved(s), d) for s, d in hip_build.SOURCES])
+    monkeypatch.setattr(hip_build, "ROOT", other)
+    assert any(f.startswith(other) for f in hip_build.FLAGS)
+    assert bench.kernel_source_hash() == base
