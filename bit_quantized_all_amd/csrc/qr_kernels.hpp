@@ -106,12 +106,18 @@ namespace qr {
 #ifndef QR_RED_GROUPS_PER_CU
 #define QR_RED_GROUPS_PER_CU 4
 #endif
-// 1: the reduce decodes its ranks in load order (each rank's codes pass an
-// empty asm that depends on the previous rank's sum), so rank r's decode
-// waits only for the loads of ranks 0..r.
+// Whether the reduce decodes its ranks in load order (each rank's codes pass
+// an empty asm that depends on the previous rank's sum), so that rank r's
+// decode waits only for the loads of ranks 0..r: 0 never, 1 for INT3 inputs
+// only, 2 always.  Without it the scheduler hoists every rank's bit-plane
+// gathers above the first sum; for INT3 R = 2 (134M fp16 values per rank)
+// the order is 0.3-0.6% faster, for the INT4, FP4 and INT4 -> INT8 R = 8
+// reduces 0.2-0.7% slower, for ASYM4 even.
 #ifndef QR_RED_RANK_ORDER
 #define QR_RED_RANK_ORDER 1
 #endif
+template <int BI>
+constexpr bool kRankOrder = QR_RED_RANK_ORDER == 2 || (QR_RED_RANK_ORDER == 1 && Format<BI>::kCodeBits == 3);
 // Encode workgroups resident on one CU at a time.  Every encode wave has its
 // whole 4 KB input tile in flight at once; a full CU (8 workgroups, 32 waves)
 // keeps more requests outstanding than HBM serves best, and 5 workgroups
@@ -158,6 +164,12 @@ constexpr int kDecLdsChunks = lds_chunks(kTileSlots, QR_DEC_GROUPS_PER_CU_MAX);
 #ifndef QR_XCD_PAIRS
 #define QR_XCD_PAIRS 1
 #endif
+// The same for the encode (1), or dispatch order there (0): the pairing made
+// the ASYM4 encode 1.1% slower (53.29 -> 52.71 us per 134M fp16 values
+// without it); the reduce keeps it (154.8 -> 154.2 us with it).
+#ifndef QR_ENC_XCD_PAIRS
+#define QR_ENC_XCD_PAIRS 0
+#endif
 
 // Index, in tile order, of workgroup b of a grid of `grid`.  Workgroups are
 // dealt to the 8 XCDs in turn (workgroup b runs on XCD b % 8), each with its
@@ -167,9 +179,9 @@ constexpr int kDecLdsChunks = lds_chunks(kTileSlots, QR_DEC_GROUPS_PER_CU_MAX);
 // each) that cover such a group are then workgroups b and b + 8 of a window of
 // 16, which run on one XCD, so that no line is split between two L2s.  The
 // last, partial window keeps the dispatch order.
-template <int TB1, int TB2>
+template <int TB1, int TB2, bool PAIRS = QR_XCD_PAIRS>
 __device__ __forceinline__ int group_index(int b, int grid) {
-  if constexpr (!QR_XCD_PAIRS || kWavesPerGroup != 4 || (TB1 % 128 == 0 && TB2 % 128 == 0)) {
+  if constexpr (!PAIRS || kWavesPerGroup != 4 || (TB1 % 128 == 0 && TB2 % 128 == 0)) {
     return b;
   } else {
     static_assert((8 * TB1) % 128 == 0 && (8 * TB2) % 128 == 0, "8 tiles span whole lines");
@@ -193,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint8_t* __restr
   u32x4* tl = lds[wave];
   const int stride = gridDim.x * kWavesPerGroup;
   constexpr int TB = Format<BITS>::kTileBytes;
-  int tile = group_index<TB, TB>(blockIdx.x, gridDim.x) * kWavesPerGroup + wave;
+  int tile = group_index<TB, TB, QR_XCD_PAIRS && QR_ENC_XCD_PAIRS>(blockIdx.x, gridDim.x) * kWavesPerGroup + wave;
   if (tile >= ntiles) return;
   // the next tile's 4 KB is loaded into registers while this one is encoded
   u32x4 v[4];
@@ -429,7 +441,7 @@ __device__ __forceinline__ void reduce_tile(const ReduceArgs& a, int tile, uint3
   for (int r = 0; r < R; ++r) {
     // rank r's codes enter its decode only after rank r - 1 is summed, so the
     // decodes run in load order and each waits only for its own loads
-    if constexpr (QR_RED_RANK_ORDER)
+    if constexpr (kRankOrder<BI>)
       if (r > 0) order_after(blk[r], sc[r], s[kBlockValues - 1]);
     if constexpr (kStaged<BI>) stage_codes_in(tl, lane, blk[r]);
     float kk[kBlockValues];
