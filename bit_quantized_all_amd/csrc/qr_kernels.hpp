@@ -106,18 +106,33 @@ namespace qr {
 #ifndef QR_RED_GROUPS_PER_CU
 #define QR_RED_GROUPS_PER_CU 4
 #endif
-// Whether the reduce decodes its ranks in load order (each rank's codes pass
-// an empty asm that depends on the previous rank's sum), so that rank r's
-// decode waits only for the loads of ranks 0..r: 0 never, 1 for INT3 inputs
-// only, 2 always.  Without it the scheduler hoists every rank's bit-plane
-// gathers above the first sum; for INT3 R = 2 (134M fp16 values per rank)
-// the order is 0.3-0.6% faster, for the INT4, FP4 and INT4 -> INT8 R = 8
-// reduces 0.2-0.7% slower, for ASYM4 even.
+// Rank-ordered decode: each rank's codes pass an empty asm that depends on
+// the previous rank's last running sum, so rank r's decode waits only for the
+// loads of ranks 0..r (without it the scheduler hoists every rank's code
+// unpacking above the first sum and each wave waits for all its loads at
+// once).  It pays when a launch has few waves per SIMD to hide that wait and
+// costs a little when it has many.  Measured, reduce per launch, 8 ranks:
+//   INT4 (fp16)   8192 tiles 23.6 -> 22.8 us ordered, 16384 41.4 -> 41.0,
+//                 32768 78.2 -> 78.3, 65536 (134M values) 150.8 -> 152.0
+//   INT4 -> INT8  8192 tiles 24.8 -> 24.4;   INT8 (R = 4) 8192 22.99 -> 22.72
+//   FP4           8192 tiles 21.9 -> 22.1;   ASYM4 even
+//   INT3 R = 2    65536 tiles 72.4 -> 72.0 (INT3 unpacks two bit planes)
+// QR_RED_RANK_ORDER: 0 never, 2 always, 1 (default) INT3 inputs always and
+// INT4 / INT8 inputs up to QR_RED_ORDER_MAX_TILES tiles.
 #ifndef QR_RED_RANK_ORDER
 #define QR_RED_RANK_ORDER 1
 #endif
+#ifndef QR_RED_ORDER_MAX_TILES
+#define QR_RED_ORDER_MAX_TILES 16384
+#endif
+// 0: the reduce of input format BI is never ordered, 1: always, 2: by size.
 template <int BI>
-constexpr bool kRankOrder = QR_RED_RANK_ORDER == 2 || (QR_RED_RANK_ORDER == 1 && Format<BI>::kCodeBits == 3);
+constexpr int kOrderMode =
+    QR_RED_RANK_ORDER == 0   ? 0
+    : QR_RED_RANK_ORDER == 2 ? 1
+    : Format<BI>::kCodeBits == 3 ? 1
+    : (!Format<BI>::kAsym && !Format<BI>::kFp4) ? 2
+                                                : 0;
 // Encode workgroups resident on one CU at a time.  Every encode wave has its
 // whole 4 KB input tile in flight at once; a full CU (8 workgroups, 32 waves)
 // keeps more requests outstanding than HBM serves best, and 5 workgroups
@@ -430,7 +445,7 @@ __device__ __forceinline__ void order_after(CodeBlock<CB>& blk, uint32_t& sc, fl
 
 // The reduction of one tile whose R blocks are in registers: exact decode,
 // fp32 rank-order sum, re-encode into packed_out and (WITH_Y) decode into y.
-template <int BI, int BO, int DT, int R, bool WITH_Y>
+template <int BI, int BO, int DT, int R, bool WITH_Y, bool ORDER>
 __device__ __forceinline__ void reduce_tile(const ReduceArgs& a, int tile, uint32_t lane, u32x4* tl,
                                             Block<BI> (&blk)[R], uint32_t (&sc)[R]) {
   constexpr int TBO = Format<BO>::kTileBytes;   // re-encoded tiles
@@ -441,7 +456,7 @@ __device__ __forceinline__ void reduce_tile(const ReduceArgs& a, int tile, uint3
   for (int r = 0; r < R; ++r) {
     // rank r's codes enter its decode only after rank r - 1 is summed, so the
     // decodes run in load order and each waits only for its own loads
-    if constexpr (kRankOrder<BI>)
+    if constexpr (ORDER)
       if (r > 0) order_after(blk[r], sc[r], s[kBlockValues - 1]);
     if constexpr (kStaged<BI>) stage_codes_in(tl, lane, blk[r]);
     float kk[kBlockValues];
@@ -586,7 +601,7 @@ __device__ __forceinline__ void reduce_tile(const ReduceArgs& a, int tile, uint3
 template <int BI, int R>
 constexpr bool kLoadsFirst = QR_RED_LOADS_FIRST && R * (int)(sizeof(Block<BI>) / 4 + 1) <= QR_RED_LOADS_FIRST_REGS;
 
-template <int BI, int BO, int DT, int R, bool WITH_Y>
+template <int BI, int BO, int DT, int R, bool WITH_Y, bool ORDER>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
   static_assert(Format<BI>::kAsym == Format<BO>::kAsym && Format<BI>::kFp4 == Format<BO>::kFp4,
                 "a reduce stays within one format family");
@@ -608,14 +623,14 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
       const bool more = next < a.ntiles;
       if (more) load_ranks<BI, R>(a, next, lane, bb, sb);
       __builtin_amdgcn_sched_barrier(0);
-      reduce_tile<BI, BO, DT, R, WITH_Y>(a, tile, lane, lds[wave], ba, sa);
+      reduce_tile<BI, BO, DT, R, WITH_Y, ORDER>(a, tile, lane, lds[wave], ba, sa);
       if (!more) break;
       tile = next;
       next = tile + stride;
       const bool more2 = next < a.ntiles;
       if (more2) load_ranks<BI, R>(a, next, lane, ba, sa);
       __builtin_amdgcn_sched_barrier(0);
-      reduce_tile<BI, BO, DT, R, WITH_Y>(a, tile, lane, lds[wave], bb, sb);
+      reduce_tile<BI, BO, DT, R, WITH_Y, ORDER>(a, tile, lane, lds[wave], bb, sb);
       if (!more2) break;
       tile = next;
     }
@@ -637,7 +652,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
         load_ranks<BI, R>(a, tile, lane, blk, sc);
         if constexpr (kLoadsFirst<BI, R>) __builtin_amdgcn_sched_barrier(0);
       }
-      reduce_tile<BI, BO, DT, R, WITH_Y>(a, tile, lane, lds[wave], blk, sc);
+      reduce_tile<BI, BO, DT, R, WITH_Y, ORDER>(a, tile, lane, lds[wave], blk, sc);
     }
   }
 }
@@ -690,10 +705,20 @@ qr_status launch_decode(int dt, const void* p, void* y, size_t ntiles, hipStream
   return k(grid_for(ntiles), st, (const uint8_t*)p, (uint8_t*)y, (int)ntiles);
 }
 
+template <int BI, int BO, int DT, int R, bool ORDER>
+qr_status launch_reduce_o(const ReduceArgs& a, dim3 grid, hipStream_t st) {
+  auto k = a.y ? launch(reduce_kernel<BI, BO, DT, R, true, ORDER>) : launch(reduce_kernel<BI, BO, DT, R, false, ORDER>);
+  return k(grid, st, a);
+}
+
 template <int BI, int BO, int DT, int R>
 qr_status launch_reduce_r(const ReduceArgs& a, dim3 grid, hipStream_t st) {
-  auto k = a.y ? launch(reduce_kernel<BI, BO, DT, R, true>) : launch(reduce_kernel<BI, BO, DT, R, false>);
-  return k(grid, st, a);
+  if constexpr (kOrderMode<BI> == 2) {
+    if (a.ntiles <= QR_RED_ORDER_MAX_TILES) return launch_reduce_o<BI, BO, DT, R, true>(a, grid, st);
+    return launch_reduce_o<BI, BO, DT, R, false>(a, grid, st);
+  } else {
+    return launch_reduce_o<BI, BO, DT, R, kOrderMode<BI> == 1>(a, grid, st);
+  }
 }
 
 template <int BI, int BO, int DT>

@@ -402,6 +402,26 @@ def test_reduce_mixed_parity(qa, oracle, fi, fo, dtype, R):
     assert np.array_equal(out2.cpu().numpy(), wout)
 
 
+@pytest.mark.parametrize("fi,fo", [("int4", "int4"), ("int8", "int8"), ("int4", "int8")])
+@pytest.mark.parametrize("ntiles", [16384, 16385])
+def test_reduce_both_sides_of_the_decode_order_switch(qa, oracle, fi, fo, ntiles):
+    """INT4 and INT8 inputs reduce with rank-ordered decodes up to 16384 tiles
+    and unordered ones above (a launch-time choice between two kernels): both
+    sides, every byte against the oracle."""
+    n = ntiles * 2048
+    R = 3
+    kinds = ["normal", "outliers", "scales"]
+    xs = [gen(kinds[r], "fp16", n, seed=5 * ntiles + r) for r in range(R)]
+    log(f"reduce {fi}->{fo} fp16 R={R} tiles={ntiles}")
+    packed = [qa.qr_encode(fi, dev(x, torch.float16)) for x in xs]
+    out, y = qa.qr_reduce_compressed_mixed(fi, fo, torch.float16, packed, n)
+    torch.cuda.synchronize()
+    wranks = [oracle.encode(BITS[fi], "fp16", x) for x in xs]
+    wout, wy = oracle.reduce_mixed(BITS[fi], BITS[fo], "fp16", wranks, n)
+    assert np.array_equal(out.cpu().numpy(), wout)
+    assert np.array_equal(u16(y), wy)
+
+
 def test_empty_calls_are_size_errors(qa):
     """n = 0 through every entry point: rejected with QR_ERR_SIZE on the host
     (the tile is the unit), nothing is launched."""
