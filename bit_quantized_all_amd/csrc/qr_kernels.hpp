@@ -162,17 +162,20 @@ constexpr int kThreads = kWave * kWavesPerGroup;
 constexpr int kMaxGroups = QR_MAX_GROUPS;
 constexpr int kLdsBytesPerCU = 160 * 1024;
 
-// 16-byte LDS chunks per wave for a kernel that needs `needed` of them and
-// may have at most `groups` workgroups on one CU (0: no limit): the whole
-// 1 / groups share of the CU's LDS when that is more than it needs, so that
-// no further workgroup fits.
-constexpr int lds_chunks(int needed, int groups) {
-  return groups > 0 && kLdsBytesPerCU / groups / (16 * kWavesPerGroup) > needed
-             ? kLdsBytesPerCU / groups / (16 * kWavesPerGroup)
-             : needed;
-}
-constexpr int kEncLdsChunks = lds_chunks(kTileSlots, QR_ENC_GROUPS_PER_CU);
-constexpr int kDecLdsChunks = lds_chunks(kTileSlots, QR_DEC_GROUPS_PER_CU_MAX);
+// The caps above apply to launches of more than QR_CAP_MIN_GROUPS workgroups
+// per CU.  A smaller grid runs in at most two generations of full residency,
+// and there a cap only adds generations: 8192 tiles (8 workgroups per CU)
+// encode in 8.5 us uncapped against 9.1 us at 5, and decode in 7.4 against
+// 9.3 us (INT4 fp16); at 16384 tiles uncapped is 0.6% (encode) and 1.3%
+// (decode) faster.
+#ifndef QR_CAP_MIN_GROUPS
+#define QR_CAP_MIN_GROUPS 16
+#endif
+
+// 16-byte LDS chunks per wave that the encode and decode kernels use (the
+// wave's tile); a residency cap adds dynamic LDS at launch (residency_pad()).
+constexpr int kEncLdsChunks = kTileSlots;
+constexpr int kDecLdsChunks = kTileSlots;
 
 // 1: workgroups of formats whose tiles are not whole 128-byte cache lines
 // take their tiles in XCD pairs (group_index()); 0: in dispatch order.
@@ -414,10 +417,9 @@ struct ReduceArgs {
 // LDS chunks per reduce wave: the fp16/bf16 output tile (WITH_Y) and / or the
 // 2 KB staging region of 8-bit codes, which reuses the output tile's space.
 template <int BI, int BO, bool WITH_Y>
-constexpr int kReduceLdsChunks = lds_chunks(
+constexpr int kReduceLdsChunks =
     WITH_Y ? kTileSlots
-           : ((kStaged<BI> || kStaged<BO>) ? kStageSlots : ((Format<BI>::kCodeBits == 3 && QR_INT3_LDS_STAGE) ? 64 : 1)),
-    QR_RED_GROUPS_PER_CU_MAX);
+           : ((kStaged<BI> || kStaged<BO>) ? kStageSlots : ((Format<BI>::kCodeBits == 3 && QR_INT3_LDS_STAGE) ? 64 : 1));
 
 // Every rank's block `lane` of tile `tile` (codes and scale) into registers.
 template <int BI, int R>
@@ -672,12 +674,14 @@ inline dim3 grid_for(size_t ntiles) {
 // of that launch itself (hipGetLastError could also report an earlier failure
 // of an unrelated call on the same thread).  The parameter types come from the
 // kernel alone, so each argument is converted to its parameter's type.
+// `lds` bytes of dynamic LDS are allocated per workgroup (the kernels never
+// address them: they only limit residency, see residency_pad()).
 template <typename... P>
 struct Launch {
   void (*kernel)(P...);
-  qr_status operator()(dim3 grid, hipStream_t st, P... args) const {
+  qr_status operator()(dim3 grid, unsigned lds, hipStream_t st, P... args) const {
     void* argv[] = {static_cast<void*>(&args)...};
-    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(kThreads), argv, 0, st) ==
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(kThreads), argv, lds, st) ==
                    hipSuccess
                ? QR_OK
                : QR_ERR_HIP;
@@ -688,27 +692,55 @@ Launch<P...> launch(void (*kernel)(P...)) {
   return {kernel};
 }
 
+// Compute units of the current device (qr_api.hip; 0 if it cannot be queried).
+int device_compute_units();
+
+// Dynamic LDS bytes per workgroup that leave room for at most `groups`
+// workgroups of a kernel with `static_bytes` of LDS on one CU, or 0 (no cap):
+// when `groups` is 0, or the grid of `nwg` workgroups has at most
+// QR_CAP_MIN_GROUPS per CU.
+inline unsigned residency_pad(unsigned nwg, int static_bytes, int groups) {
+  if (groups <= 0) return 0;
+  const int cus = device_compute_units();
+  if (cus <= 0 || nwg <= (unsigned)cus * QR_CAP_MIN_GROUPS) return 0;
+  const int per_group = kLdsBytesPerCU / groups;
+  return per_group > static_bytes ? (unsigned)(per_group - static_bytes) : 0u;
+}
+
 template <int BITS>
 qr_status launch_encode(int dt, const void* x, void* p, size_t ntiles, hipStream_t st) {
+  constexpr int kStatic = kWavesPerGroup * kEncLdsChunks * 16;
   if constexpr (QR_ENC_GROUP8 && (BITS == 3 || BITS == 4)) {
+    const dim3 grid = grid_for(ntiles);
     auto k = dt == kFp16 ? launch(encode_group8_kernel<BITS, kFp16>) : launch(encode_group8_kernel<BITS, kBf16>);
-    return k(grid_for(ntiles), st, (const uint8_t*)x, (uint8_t*)p, (int)ntiles);
+    return k(grid, residency_pad(grid.x, kStatic, QR_ENC_GROUPS_PER_CU), st, (const uint8_t*)x, (uint8_t*)p,
+             (int)ntiles);
   }
   const dim3 grid = grid_for((ntiles + QR_ENC_TILES_PER_WAVE - 1) / QR_ENC_TILES_PER_WAVE);
   auto k = dt == kFp16 ? launch(encode_kernel<BITS, kFp16>) : launch(encode_kernel<BITS, kBf16>);
-  return k(grid, st, (const uint8_t*)x, (uint8_t*)p, (int)ntiles);
+  return k(grid, residency_pad(grid.x, kStatic, QR_ENC_GROUPS_PER_CU), st, (const uint8_t*)x, (uint8_t*)p,
+           (int)ntiles);
 }
 
 template <int BITS>
 qr_status launch_decode(int dt, const void* p, void* y, size_t ntiles, hipStream_t st) {
+  constexpr int kStatic = kWavesPerGroup * kDecLdsChunks * 16;
+  const dim3 grid = grid_for(ntiles);
   auto k = dt == kFp16 ? launch(decode_kernel<BITS, kFp16>) : launch(decode_kernel<BITS, kBf16>);
-  return k(grid_for(ntiles), st, (const uint8_t*)p, (uint8_t*)y, (int)ntiles);
+  return k(grid, residency_pad(grid.x, kStatic, QR_DEC_GROUPS_PER_CU_MAX), st, (const uint8_t*)p, (uint8_t*)y,
+           (int)ntiles);
 }
 
 template <int BI, int BO, int DT, int R, bool ORDER>
 qr_status launch_reduce_o(const ReduceArgs& a, dim3 grid, hipStream_t st) {
-  auto k = a.y ? launch(reduce_kernel<BI, BO, DT, R, true, ORDER>) : launch(reduce_kernel<BI, BO, DT, R, false, ORDER>);
-  return k(grid, st, a);
+  if (a.y) {
+    constexpr int kStatic = kWavesPerGroup * kReduceLdsChunks<BI, BO, true> * 16;
+    return launch(reduce_kernel<BI, BO, DT, R, true, ORDER>)(
+        grid, residency_pad(grid.x, kStatic, QR_RED_GROUPS_PER_CU_MAX), st, a);
+  }
+  constexpr int kStatic = kWavesPerGroup * kReduceLdsChunks<BI, BO, false> * 16;
+  return launch(reduce_kernel<BI, BO, DT, R, false, ORDER>)(
+      grid, residency_pad(grid.x, kStatic, QR_RED_GROUPS_PER_CU_MAX), st, a);
 }
 
 template <int BI, int BO, int DT, int R>
@@ -734,9 +766,6 @@ qr_status launch_reduce_dt(const ReduceArgs& a, dim3 grid, hipStream_t st) {
     default: return QR_ERR_ARG;  // R is validated to be in [1, QR_MAX_RANKS] before this
   }
 }
-
-// Compute units of the current device (qr_api.hip; 0 if it cannot be queried).
-int device_compute_units();
 
 // Reduce grid: one wave per tile, or with QR_RED_PREFETCH at most
 // QR_RED_GROUPS_PER_CU workgroups per compute unit, each wave looping.
