@@ -700,14 +700,11 @@ __device__ __forceinline__ uint32_t quantize_words_asym(const uint32_t (&w)[kBlo
 //          and 5 as 1024 + 16q (minus 1024 + 16z: 16(q - z)); the word
 //          shifted right by 8 gives values 2, 6 and 3, 7 the same way.
 //   8-bit: byte gathers put codes 0, 2 and 1, 3 of a word under a 0x64 byte.
+// nz and nzo are the fp16 pairs -(1024 + z) and -(1024 + 16 z) (AsymMeta).
 template <int F>
-__device__ __forceinline__ void decode_block_asym(const Block<F>& blk, uint32_t z, float (&kk)[kBlockValues]) {
-  // -(1024 + c) for an integer 0 <= c < 1024 is the fp16 pattern 0xE400 | c
-  const uint32_t nzb = 0xE400u | z;
-  const f16x2 nz = __builtin_bit_cast(f16x2, nzb | (nzb << 16));
+__device__ __forceinline__ void decode_block_asym(const Block<F>& blk, f16x2 nz, f16x2 nzo,
+                                                  float (&kk)[kBlockValues]) {
   if constexpr (Format<F>::kCodeBits == 4) {
-    const uint32_t nzob = 0xE400u | (z << 4);
-    const f16x2 nzo = __builtin_bit_cast(f16x2, nzob | (nzob << 16));
     const uint32_t m0 = vgpr_const(0x000F000Fu), m1 = vgpr_const(0x00F000F0u);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -887,15 +884,42 @@ __device__ __forceinline__ void stage_int3_in(u32x4* tl, uint32_t g, u32x4 raw, 
   scale = s;
 }
 
-// Scale bits | zero point << 16 of the group of lane g's block, from the
-// dwords load_block() left in the lanes: dwords 0..7 hold the 16 fp16 scales
-// (two each), dwords 8..11 the 16 zero points (four each).  Every lane of the
-// wave takes part (cross-lane permutes).
-__device__ __forceinline__ uint32_t group_meta(uint32_t m, int g) {
-  const int grp = g >> 2;
-  const uint32_t sdw = (uint32_t)__builtin_amdgcn_ds_bpermute((grp >> 1) << 2, (int)m);
-  const uint32_t zdw = (uint32_t)__builtin_amdgcn_ds_bpermute((8 + (grp >> 2)) << 2, (int)m);
-  return ((sdw >> (16 * (grp & 1))) & 0xffffu) | (((zdw >> (8 * (grp & 3))) & 0xffu) << 16);
+// What the decode of lane g's block needs from its group's scale s and zero
+// point z: s for even values and s * 2^-kOddShift for odd ones (fp32), and the
+// fp16 pairs -(1024 + z) and -(1024 + 16 z) (the pattern 0xE400 | c is
+// -(1024 + c) for c < 1024).
+struct AsymMeta {
+  float d, dodd;
+  f16x2 nz, nzo;
+};
+
+// Byte selectors (v_perm_b32) that pick lane g's group out of the two dwords
+// group_meta() fetches: the scale's two bytes, and z under 0xE4 bytes twice.
+struct MetaSel {
+  uint32_t scale, zero;
+};
+__device__ __forceinline__ MetaSel meta_sel(uint32_t g) {
+  const uint32_t grp = g >> 2, sb = 2 * (grp & 1), zb = grp & 3;
+  return {sb | ((sb + 1) << 8) | 0x0C0C0000u, zb | (4u << 8) | (zb << 16) | (4u << 24)};
+}
+
+// The group metadata of lane g's block, from the dwords load_block() left in
+// the lanes: dwords 0..7 hold the 16 fp16 scales (two each), dwords 8..11 the
+// 16 zero points (four each).  Every lane of the wave takes part (cross-lane
+// permutes).
+template <int F>
+__device__ __forceinline__ AsymMeta group_meta(uint32_t m, uint32_t g, const MetaSel& sel) {
+  const uint32_t grp = g >> 2;
+  const uint32_t sdw = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((grp >> 1) << 2), (int)m);
+  const uint32_t zdw = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((8 + (grp >> 2)) << 2), (int)m);
+  constexpr uint32_t kE4 = 0xE4E4E4E4u;
+  AsymMeta a;
+  a.d = (float)__builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_perm(sdw, sdw, sel.scale));
+  a.dodd = a.d * (1.0f / (1 << Format<F>::kOddShift));
+  a.nz = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kE4, zdw, sel.zero));
+  // 4-bit zero points: z << 4 stays within its byte
+  a.nzo = Format<F>::kOddShift ? __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kE4, zdw << 4, sel.zero)) : a.nz;
+  return a;
 }
 
 // Stores block g; for the asymmetric formats the first lane of each group

@@ -382,10 +382,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint8_t* __restr
     float kk[kBlockValues];
     float dd, ddo;  // scales of even and odd values
     if constexpr (Format<BITS>::kAsym) {
-      scale = group_meta(scale, lane);
-      decode_block_asym<BITS>(blk, scale >> 16, kk);
-      dd = scale_f32(scale);
-      ddo = dd * (1.0f / (1 << Format<BITS>::kOddShift));
+      const AsymMeta am = group_meta<BITS>(scale, lane, meta_sel(lane));
+      decode_block_asym<BITS>(blk, am.nz, am.nzo, kk);
+      dd = am.d;
+      ddo = am.dodd;
     } else if constexpr (Format<BITS>::kFp4) {
       decode_block_fp4(blk, kk);
       dd = ddo = scale_f32(scale);
@@ -464,10 +464,10 @@ __device__ __forceinline__ void reduce_tile(const ReduceArgs& a, int tile, uint3
     float kk[kBlockValues];
     float dd, ddo;  // scales of even and odd values (exact products with kk)
     if constexpr (Format<BI>::kAsym) {
-      sc[r] = group_meta(sc[r], lane);
-      decode_block_asym<BI>(blk[r], sc[r] >> 16, kk);
-      dd = scale_f32(sc[r]);
-      ddo = dd * (1.0f / (1 << Format<BI>::kOddShift));
+      const AsymMeta am = group_meta<BI>(sc[r], lane, meta_sel(lane));
+      decode_block_asym<BI>(blk[r], am.nz, am.nzo, kk);
+      dd = am.d;
+      ddo = am.dodd;
     } else if constexpr (Format<BI>::kFp4) {
       decode_block_fp4(blk[r], kk);
       dd = ddo = scale_f32(sc[r]);
