@@ -152,6 +152,12 @@ constexpr int kOrderMode =
 #ifndef QR_RED_GROUPS_PER_CU_MAX
 #define QR_RED_GROUPS_PER_CU_MAX 5
 #endif
+// The same for reduces of 8-bit inputs, whose waves each have twice the
+// input bytes in flight: INT8 R = 4, 268M fp16 values per rank, 315.7 ->
+// 310.3 us at 3 workgroups (4: 315.3); 67M values 79.7 -> 79.3 us.
+#ifndef QR_RED8_GROUPS_PER_CU_MAX
+#define QR_RED8_GROUPS_PER_CU_MAX 3
+#endif
 // Decode workgroups resident on one CU at a time (0: no limit); per
 // 134M-value INT4 fp16 rank 56.4 -> 53.8 us at 5 workgroups (20 waves).
 #ifndef QR_DEC_GROUPS_PER_CU_MAX
@@ -733,14 +739,13 @@ qr_status launch_decode(int dt, const void* p, void* y, size_t ntiles, hipStream
 
 template <int BI, int BO, int DT, int R, bool ORDER>
 qr_status launch_reduce_o(const ReduceArgs& a, dim3 grid, hipStream_t st) {
+  constexpr int kCap = kStaged<BI> ? QR_RED8_GROUPS_PER_CU_MAX : QR_RED_GROUPS_PER_CU_MAX;
   if (a.y) {
     constexpr int kStatic = kWavesPerGroup * kReduceLdsChunks<BI, BO, true> * 16;
-    return launch(reduce_kernel<BI, BO, DT, R, true, ORDER>)(
-        grid, residency_pad(grid.x, kStatic, QR_RED_GROUPS_PER_CU_MAX), st, a);
+    return launch(reduce_kernel<BI, BO, DT, R, true, ORDER>)(grid, residency_pad(grid.x, kStatic, kCap), st, a);
   }
   constexpr int kStatic = kWavesPerGroup * kReduceLdsChunks<BI, BO, false> * 16;
-  return launch(reduce_kernel<BI, BO, DT, R, false, ORDER>)(
-      grid, residency_pad(grid.x, kStatic, QR_RED_GROUPS_PER_CU_MAX), st, a);
+  return launch(reduce_kernel<BI, BO, DT, R, false, ORDER>)(grid, residency_pad(grid.x, kStatic, kCap), st, a);
 }
 
 template <int BI, int BO, int DT, int R>
