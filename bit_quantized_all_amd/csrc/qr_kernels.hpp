@@ -138,7 +138,9 @@ constexpr int kOrderMode =
 // keeps more requests outstanding than HBM serves best, and 5 workgroups
 // (20 waves) measured fastest: per 134M-value fp16 rank, INT4 56.9 -> 53.2 us,
 // INT3 53.9 -> 51.1 us, INT8 64.4 -> 62.6 us; 3 and 2 workgroups were slower.
-// The kernel sizes its LDS so that no more fit in the CU's 160 KB.
+// The launch adds dynamic LDS so that no more fit in the CU's 160 KB
+// (residency_pad(); caps of 3 and more, which keep a workgroup's LDS within
+// 64 KB).
 #ifndef QR_ENC_GROUPS_PER_CU
 #define QR_ENC_GROUPS_PER_CU 5
 #endif
@@ -148,7 +150,8 @@ constexpr int kOrderMode =
 // mix of reads and writes better: INT3 R = 2, 134M fp16 values per rank,
 // 74.9 -> 72.2 us at 5 workgroups (20 waves), 72.6 us at 6; INT3 R = 4 at
 // 512 MiB per rank 189.5 -> 182.3 us.  Kernels whose registers already allow
-// at most 20 waves per CU (INT4 R = 8: 16) are not affected.
+// at most 20 waves per CU (INT4 R = 8 unordered: 143 VGPRs, 12 waves) are
+// not limited further.
 #ifndef QR_RED_GROUPS_PER_CU_MAX
 #define QR_RED_GROUPS_PER_CU_MAX 5
 #endif
@@ -163,6 +166,10 @@ constexpr int kOrderMode =
 #ifndef QR_DEC_GROUPS_PER_CU_MAX
 #define QR_DEC_GROUPS_PER_CU_MAX 5
 #endif
+static_assert(QR_ENC_GROUPS_PER_CU == 0 || QR_ENC_GROUPS_PER_CU >= 3, "residency caps of 3 or more");
+static_assert(QR_RED_GROUPS_PER_CU_MAX == 0 || QR_RED_GROUPS_PER_CU_MAX >= 3, "residency caps of 3 or more");
+static_assert(QR_RED8_GROUPS_PER_CU_MAX == 0 || QR_RED8_GROUPS_PER_CU_MAX >= 3, "residency caps of 3 or more");
+static_assert(QR_DEC_GROUPS_PER_CU_MAX == 0 || QR_DEC_GROUPS_PER_CU_MAX >= 3, "residency caps of 3 or more");
 constexpr int kWavesPerGroup = QR_WAVES_PER_GROUP;
 constexpr int kThreads = kWave * kWavesPerGroup;
 constexpr int kMaxGroups = QR_MAX_GROUPS;
