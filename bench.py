@@ -294,7 +294,7 @@ def main():
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--lib", default=None,
-                    help="load this build of libqr.so instead of the package's (a compile-time variant "
+                    help="load the libqr.so at PATH instead of the package's (a compile-time variant "
                          "made with python -m bit_quantized_all_amd.build --out PATH -DNAME=VALUE)")
     args = ap.parse_args()
 

@@ -1,7 +1,7 @@
 /* validate_check.c -- every argument check of include/qr.h from plain C, with
  * no GPU work: each call is rejected on the host (n == 0 included), or
- * passes the checks and reaches a launch function that this build replaces
- * with a stand-in (launch_stubs.cpp), so the pointers below are addresses
+ * passes the checks and reaches a launch function that the test program
+ * replaces with a stand-in (launch_stubs.cpp), so the pointers below are addresses
  * that are never dereferenced.  Built against a host-sanitized (AddressSanitizer and
  * UndefinedBehaviorSanitizer) build of the C ABI.  Prints one line per
  * failure and "all checks passed" at the end; exit status 0 when every
@@ -122,8 +122,8 @@ static void reduce(void) {
   EXPECT(qr_reduce_compressed_mixed(QR_INT4, QR_INT8, QR_BF16, ranks, 1, P(D), NULL, 0, NULL), QR_ERR_SIZE);
 }
 
-/* Calls that pass every check reach the launch, which in this build is a
- * stand-in returning QR_ERR_HIP: the checks do not reject valid calls,
+/* Calls that pass every check reach the launch, which in the test program is
+ * a stand-in returning QR_ERR_HIP: the checks do not reject valid calls,
  * including buffers that touch without overlapping and repeated rank buffers. */
 static void accepted(void) {
   const size_t n = 4 * 2048;
