@@ -284,8 +284,11 @@ def test_workload_full_size_sampled(qa, oracle, name, seed):
 
 
 # Workloads whose whole full-size output is checked against the oracle, tile
-# by tile: the bench workload and the INT3 two-rank reduce.
-EVERY_TILE_CASES = ["int4_r8_fp16_32x1024x4096", "int3_r2_fp16_32x1024x4096"]
+# by tile: the bench workload, the INT3 two-rank reduce, the mixed INT4 -> INT8
+# and ASYM4 -> ASYM8 reduces, FP4, and INT8 at 512 MiB per rank (the kernels'
+# large-grid launch choices: unordered decodes, residency caps).
+EVERY_TILE_CASES = ["int4_r8_fp16_32x1024x4096", "int3_r2_fp16_32x1024x4096", "int6_r8_fp16_32x1024x4096",
+                    "asym6_r8_fp16_32x1024x4096", "fp4_r8_fp16_32x1024x4096", "sweep_r4_fp16_int8_512mib"]
 
 
 def _host_threads():
