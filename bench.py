@@ -15,6 +15,10 @@ sample of the same input.  With --graph the timed launches are captured in
 HIP graphs and replayed, which removes the host-side cost of issuing each
 launch from Python (it bounds steps on small messages).
 
+Untimed warmup: at least W whole steps, and whole steps until at least
+--min-warmup-ms (default 200) have passed; the line reports both W and the
+number of warmup steps run.
+
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--graph]
 """
 import argparse
@@ -268,6 +272,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--min-warmup-ms", type=float, default=200.0,
+                    help="after the W warmup steps, keep running untimed whole steps until this much "
+                         "time has passed since the warmup began: the first tens of milliseconds of "
+                         "full-size steps run up to 3%% slower while the GPU settles")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--values", type=int, default=None,
@@ -370,9 +378,15 @@ def main():
         torch.cuda.synchronize()
         return g.replay
 
-    for i in range(max(args.warmup, nsets)):
-        step(sets[i % nsets])
-    torch.cuda.synchronize()
+    warm_steps = 0
+    t_warm = time.perf_counter()
+    while True:
+        for _ in range(nsets):
+            step(sets[warm_steps % nsets])
+            warm_steps += 1
+        torch.cuda.synchronize()
+        if warm_steps >= args.warmup and (time.perf_counter() - t_warm) * 1e3 >= args.min_warmup_ms:
+            break
     run_steps = [runner(lambda b=b: step(b)) for b in sets]
     for run in run_steps:
         run()
@@ -488,6 +502,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
         "ms_per_step": round(ms_per_step, 5),
         "ms_per_step_median": round(ms_median, 5),
         "higher_is_better": True,
