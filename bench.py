@@ -378,15 +378,16 @@ def main():
         torch.cuda.synchronize()
         return g.replay
 
-    warm_steps = 0
     t_warm = time.perf_counter()
-    while True:
+    warm_steps = max(args.warmup, nsets)
+    for i in range(warm_steps):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t_warm) * 1e3 < args.min_warmup_ms:
         for _ in range(nsets):
             step(sets[warm_steps % nsets])
             warm_steps += 1
         torch.cuda.synchronize()
-        if warm_steps >= args.warmup and (time.perf_counter() - t_warm) * 1e3 >= args.min_warmup_ms:
-            break
     run_steps = [runner(lambda b=b: step(b)) for b in sets]
     for run in run_steps:
         run()
