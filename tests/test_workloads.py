@@ -17,6 +17,10 @@ def test_catalogue():
     c, b = W.small(w["int4_fp16_codec_32x1024x4096"], 4096 * 4), W.small(w["int4_r8_fp16_32x1024x4096"], 4096 * 4)
     assert not c.reduce and c.ranks == 1
     assert torch.equal(W.rank_input(c, 0, seed=1).view(torch.int16), W.rank_input(b, 0, seed=1).view(torch.int16))
+    # INT3 and INT4 over two ranks see the same inputs
+    a, b = W.small(w["int3_r2_fp16_32x1024x4096"], 4096 * 4), W.small(w["int4_r2_fp16_32x1024x4096"], 4096 * 4)
+    for r in range(2):
+        assert torch.equal(W.rank_input(a, r, seed=2).view(torch.int16), W.rank_input(b, r, seed=2).view(torch.int16))
     for v in w.values():
         assert v.n % 2048 == 0
 

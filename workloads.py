@@ -33,6 +33,8 @@ tiles):
                            activations (same channel spread, its own streams).
   int3_r2_fp16_32x1024x4096  INT3 over R=2 ranks of the same shape and spread
                            (tensor parallelism 2, where the pages recommend INT3).
+  int4_r2_fp16_32x1024x4096  INT4 on the same two ranks' inputs (INT3 against
+                           INT4 at tensor parallelism 2, same data).
   int4_fp16_codec_32x1024x4096  encode + decode only of rank 0's input of the
                            [32 x 1024 x 4096] INT4 workload (the receive side's
                            decode of gathered tiles, at full size).
@@ -123,6 +125,10 @@ WORKLOADS = {
     # INT3 over two ranks (tensor parallelism 2, where the pages recommend INT3)
     "int3_r2_fp16_32x1024x4096": Workload("int3_r2_fp16_32x1024x4096", "int3", torch.float16, 2,
                                           32 * 1024 * 4096, (32, 1024, 4096), channel_sigma=(0.01, 20.0)),
+    # INT4 on the INT3 two-rank workload's inputs
+    "int4_r2_fp16_32x1024x4096": Workload("int4_r2_fp16_32x1024x4096", "int4", torch.float16, 2,
+                                          32 * 1024 * 4096, (32, 1024, 4096), channel_sigma=(0.01, 20.0),
+                                          data_key="int3_r2_fp16_32x1024x4096"),
     # encode + decode only, on rank 0's input of the INT4 R=8 workload
     "int4_fp16_codec_32x1024x4096": Workload("int4_fp16_codec_32x1024x4096", "int4", torch.float16, 1,
                                              32 * 1024 * 4096, (32, 1024, 4096),
